@@ -1,0 +1,174 @@
+/*
+ * tg_gemm.h -- C ABI of the MI355X (gfx950) GEMM library libtg_gemm.so.
+ *
+ * Operation ("Matrix Multiplication Background User's Guide", sections 1-2,
+ * in BLAS naming: A is M x K, B is K x N, C is M x N):
+ *
+ *     C[i][j] = epi( sum_{k < K} A(i,k) * B(k,j) )        (C is overwritten)
+ *
+ * All matrices are row-major.  An operand may be stored transposed, as the
+ * row-major array of its transpose (what the Triton matmul tutorial's
+ * Y.T.contiguous() produces, "Learning Triton One Kernel at a Time: Matrix
+ * Multiplication", section on memory coalescing):
+ *
+ *     A(i,k) = (trans & TG_TRANS_A) ? A[k*lda + i] : A[i*lda + k]
+ *     B(k,j) = (trans & TG_TRANS_B) ? B[j*ldb + k] : B[k*ldb + j]
+ *     C(i,j) = C[i*ldc + j]
+ *
+ * Inputs and output share one storage type (dtype); products are accumulated
+ * in float32 and the epilogue is applied to the float32 sum before the single
+ * rounding (nearest-even) to the output type.  The optional epilogue is a
+ * leaky rectifier x >= 0 ? x : slope*x, the fused output transform the
+ * Triton news article gives as the reason to hand-write matmul kernels
+ * ("OpenAI open-sources Triton", matrix multiplication section).
+ *
+ * Leading dimensions (element counts):
+ *     lda >= max(1, trans_a ? M : K),  ldb >= max(1, trans_b ? K : N),
+ *     ldc >= max(1, N).
+ * Strided views (an operand that is a slice of a wider matrix) are passed as
+ * ld > width.  Misaligned pointers or leading dimensions are not errors; they
+ * select a slower element-wise load path.
+ *
+ * Ownership and ordering: every pointer is caller-owned device memory; the
+ * library keeps none of them after returning.  Work is enqueued on `stream`
+ * (a hipStream_t; NULL = the null stream) and the call returns without
+ * waiting: results are valid once the stream has been synchronised.  C must
+ * not overlap A or B.
+ *
+ * Quick returns: M == 0 or N == 0 does nothing; K == 0 writes epi(0) = 0.
+ *
+ * Errors: every entry point returns a tg_status; on failure nothing is
+ * enqueued and tg_last_error() describes the cause (thread-local).
+ */
+#ifndef TG_GEMM_H
+#define TG_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_VERSION 100
+
+/* storage type of A, B and C */
+enum tg_dtype { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 };
+
+/* trans bits; first letter of the name is A's: TG_NT = A plain, B transposed */
+enum tg_trans { TG_NN = 0, TG_TN = 1, TG_NT = 2, TG_TT = 3 };
+#define TG_TRANS_A 1
+#define TG_TRANS_B 2
+
+enum tg_epi_kind { TG_EPI_NONE = 0, TG_EPI_LEAKY_RELU = 1 };
+
+enum tg_status {
+    TG_OK = 0,
+    TG_ERR_ARG = -1,         /* negative size, leading dimension too small, unknown enum */
+    TG_ERR_NULL = -2,        /* NULL pointer for an operand that has elements */
+    TG_ERR_UNSUPPORTED = -3, /* a forced option that no kernel implements */
+    TG_ERR_DEVICE = -4,      /* no gfx950 device, or a HIP runtime error */
+    TG_ERR_LAUNCH = -5       /* a kernel launch failed */
+};
+
+/* Execution paths.  The planner picks one per call ("Matrix Multiplication
+ * Background User's Guide", section 2: the arithmetic-intensity test decides
+ * between math-bound and memory-bound; section 2.3: a library heuristic picks
+ * the tile, and splits K when M and N are small and K is large). */
+enum tg_path {
+    TG_PATH_AUTO = -1,
+    TG_PATH_NONE = 0,   /* quick return (M == 0, N == 0) or K == 0 fill */
+    TG_PATH_MFMA = 1,   /* macro-tile matrix-core kernel (all storage types) */
+    TG_PATH_SKINNY = 2, /* memory-bound narrow product (small N or small M), matrix cores */
+    TG_PATH_GEMV = 3    /* M == 1 or N == 1: vector ALUs, no matrix cores */
+};
+
+typedef struct tg_epilogue {
+    uint32_t kind; /* tg_epi_kind */
+    float slope;   /* negative-side slope of TG_EPI_LEAKY_RELU */
+} tg_epilogue;
+
+/* Optional planner overrides (NULL = all automatic).  A forced tile reproduces
+ * the forced-tile measurements of "Matrix Multiplication Background User's
+ * Guide", sections 3.1-3.2. */
+typedef struct tg_options {
+    int32_t path;    /* TG_PATH_AUTO, or a forced path */
+    int32_t tile_m;  /* 0 = planner's choice, else a macro-tile height the path offers */
+    int32_t tile_n;  /* 0 = planner's choice, else a macro-tile width */
+    int32_t split_k; /* 0 = planner's choice, 1 = no split, s > 1 = split K s ways */
+} tg_options;
+
+/* What the planner decided, and the quantization figures behind it. */
+typedef struct tg_plan {
+    int32_t path;        /* tg_path */
+    int32_t tile_m, tile_n, tile_k;
+    int32_t split_k;     /* K-splits (1 = none) */
+    int32_t occupancy;   /* workgroups resident per compute unit */
+    int32_t num_cus;     /* compute units the wave model used */
+    int32_t vector_io;   /* 1 = 128-bit operand loads, 0 = element-wise */
+    int64_t tiles;       /* ceil(M/tile_m) * ceil(N/tile_n) */
+    int64_t workgroups;  /* tiles * split_k (MFMA/skinny), or the GEMV grid */
+    int64_t waves;       /* ceil(workgroups / (num_cus * occupancy)) */
+    double tile_eff;     /* M*N / (tiles * tile_m * tile_n) */
+    double wave_eff;     /* workgroups / (waves * num_cus * occupancy) */
+    double pred_eff;     /* product of the two with the per-tile efficiency */
+    double pred_us;      /* modelled run time, microseconds */
+    double arith_intensity; /* 2MNK / (bytes of A, B and C), FLOP per byte */
+    uint64_t workspace_bytes; /* float32 split-K partials the plan needs */
+} tg_plan;
+
+/* C = epi(A . B) on the current HIP device.  epilogue may be NULL (none).
+ * When the plan splits K, float32 partials live in a stream-ordered
+ * allocation made and released by the library on `stream`. */
+int tg_gemm(int64_t M, int64_t N, int64_t K,
+            const void *A, int64_t lda,
+            const void *B, int64_t ldb,
+            void *C, int64_t ldc,
+            int dtype, int trans,
+            const tg_epilogue *epilogue,
+            void *stream);
+
+/* tg_gemm with planner overrides and a caller-provided workspace.
+ * workspace == NULL: as tg_gemm.  Otherwise it must be device memory aligned
+ * to 256 bytes; when smaller than the plan's workspace_bytes the planner
+ * falls back to an unsplit plan (not an error unless split_k was forced, then
+ * TG_ERR_ARG).  Concurrent calls must not share a workspace. */
+int tg_gemm_ex(int64_t M, int64_t N, int64_t K,
+               const void *A, int64_t lda,
+               const void *B, int64_t ldb,
+               void *C, int64_t ldc,
+               int dtype, int trans,
+               const tg_epilogue *epilogue,
+               const tg_options *opts,
+               void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/* The plan tg_gemm_ex would run on the current device (no launch). */
+int tg_gemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int trans,
+                 const tg_options *opts, tg_plan *out);
+
+/* The same planner as a pure model of a chip with num_cus compute units
+ * (no device needed).  occupancy <= 0 uses the kernels' own residency;
+ * a positive value overrides it (1 reproduces the one-tile-per-SM waves of
+ * "Matrix Multiplication Background User's Guide", section 3.2). */
+int tg_plan_model(int64_t M, int64_t N, int64_t K, int dtype, int trans,
+                  int num_cus, int occupancy, const tg_options *opts, tg_plan *out);
+
+/* Bytes of workspace the current device's plan needs (0 = none). */
+size_t tg_workspace_size(int64_t M, int64_t N, int64_t K, int dtype, int trans,
+                         const tg_options *opts);
+
+/* Compute units of the current device, or a negative tg_status. */
+int tg_device_cus(void);
+
+/* Description of the last failure on this thread ("" after success). */
+const char *tg_last_error(void);
+
+/* TG_VERSION of the built library. */
+int tg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_GEMM_H */

@@ -1,0 +1,450 @@
+// api.cpp -- the C ABI: argument checks, quick returns, planning, workspace,
+// launches and error reporting.  See include/tg_gemm.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/tg_gemm.h"
+#include "kernels/launch.hpp"
+#include "plan.h"
+
+namespace tg {
+
+// ---------------------------------------------------------------- dispatch by type
+
+hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, const MfmaArgs &a,
+                       hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F16: return launch_mfma_f16(trans, bm, bn, vec, a, s);
+    case TG_BF16: return launch_mfma_bf16(trans, bm, bn, vec, a, s);
+    case TG_F32: return launch_mfma_f32(trans, bm, bn, vec, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec)
+{
+    switch (dtype) {
+    case TG_F16: return mfma_occupancy_f16(trans, bm, bn, vec);
+    case TG_BF16: return mfma_occupancy_bf16(trans, bm, bn, vec);
+    case TG_F32: return mfma_occupancy_f32(trans, bm, bn, vec);
+    }
+    return 0;
+}
+
+hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, int N, void *C,
+                                int64_t ldc, int epi, float slope, int c_vec, hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F16: return launch_splitk_reduce_f16(ws, splits, M, N, C, ldc, epi, slope, c_vec, s);
+    case TG_BF16: return launch_splitk_reduce_bf16(ws, splits, M, N, C, ldc, epi, slope, c_vec, s);
+    case TG_F32: return launch_splitk_reduce_f32(ws, splits, M, N, C, ldc, epi, slope, c_vec, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill_zero(int dtype, void *C, int M, int N, int64_t ldc, hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F16: return launch_fill_zero_f16(C, M, N, ldc, s);
+    case TG_BF16: return launch_fill_zero_bf16(C, M, N, ldc, s);
+    case TG_F32: return launch_fill_zero_f32(C, M, N, ldc, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(int dtype, bool rows_form, bool vec, const GemvArgs &a, hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F16: return launch_gemv_f16(rows_form, vec, a, s);
+    case TG_BF16: return launch_gemv_bf16(rows_form, vec, a, s);
+    case TG_F32: return launch_gemv_f32(rows_form, vec, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- errors
+
+static thread_local std::string g_err;
+
+static int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+static int ok()
+{
+    g_err.clear();
+    return TG_OK;
+}
+
+// ---------------------------------------------------------------- device facts
+
+struct DeviceInfo {
+    bool probed = false;
+    bool gfx950 = false;
+    int cus = 0;
+    std::string arch;
+    // measured residency per (dtype, trans, tile, vec), 0 = not yet asked
+    int occ[3][4][8][2] = {};
+};
+
+static std::mutex g_dev_mu;
+static DeviceInfo g_dev[64];
+
+static int current_device(DeviceInfo **info)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        int n = 0;
+        if (hipGetDeviceCount(&n) != hipSuccess || n <= 0)
+            return fail(TG_ERR_DEVICE, "no HIP device available");
+        return fail(TG_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+    }
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(TG_ERR_DEVICE, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+        d.arch = prop.gcnArchName;
+        d.gfx950 = d.arch.compare(0, 6, "gfx950") == 0;
+        d.cus = prop.multiProcessorCount;
+        d.probed = true;
+    }
+    if (!d.gfx950)
+        return fail(TG_ERR_DEVICE, "device %d is %s; this library is built for gfx950 only", dev,
+                    d.arch.c_str());
+    *info = &d;
+    return TG_OK;
+}
+
+static int tile_slot(int bm, int bn)
+{
+    // index of the tile in a small fixed table used for the occupancy cache
+    static const int tiles[8][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64},
+                                    {64, 64},   {128, 256}, {64, 128},  {32, 32}};
+    for (int i = 0; i < 8; ++i)
+        if (tiles[i][0] == bm && tiles[i][1] == bn)
+            return i;
+    return -1;
+}
+
+static int device_occ(int dtype, int trans, int bm, int bn, bool vec, void *ctx)
+{
+    DeviceInfo *d = (DeviceInfo *)ctx;
+    const int ts = tile_slot(bm, bn);
+    if (ts < 0)
+        return model_occupancy(dtype, bm, bn, vec);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    int &slot = d->occ[dtype][trans][ts][vec ? 1 : 0];
+    if (slot == 0) {
+        int n = mfma_occupancy(dtype, trans, bm, bn, vec);
+        slot = n > 0 ? n : -1;
+    }
+    return slot > 0 ? slot : model_occupancy(dtype, bm, bn, vec);
+}
+
+// ---------------------------------------------------------------- validation
+
+static int check_args(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                      int64_t ldb, void *C, int64_t ldc, int dtype, int trans,
+                      const tg_epilogue *epi)
+{
+    if (dtype < TG_F32 || dtype > TG_BF16)
+        return fail(TG_ERR_ARG, "unknown dtype %d", dtype);
+    if (trans < 0 || trans > 3)
+        return fail(TG_ERR_ARG, "unknown trans %d", trans);
+    if (epi && epi->kind != TG_EPI_NONE && epi->kind != TG_EPI_LEAKY_RELU)
+        return fail(TG_ERR_ARG, "unknown epilogue kind %u", epi->kind);
+    if (M < 0 || N < 0 || K < 0)
+        return fail(TG_ERR_ARG, "negative dimension (M=%lld N=%lld K=%lld)", (long long)M,
+                    (long long)N, (long long)K);
+    if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+        return fail(TG_ERR_ARG, "dimension above 2^31-1");
+    const bool ta = trans & TG_TRANS_A, tb = trans & TG_TRANS_B;
+    const int64_t need_a = std::max<int64_t>(1, ta ? M : K);
+    const int64_t need_b = std::max<int64_t>(1, tb ? K : N);
+    const int64_t need_c = std::max<int64_t>(1, N);
+    if (lda < need_a)
+        return fail(TG_ERR_ARG, "lda=%lld < %lld", (long long)lda, (long long)need_a);
+    if (ldb < need_b)
+        return fail(TG_ERR_ARG, "ldb=%lld < %lld", (long long)ldb, (long long)need_b);
+    if (ldc < need_c)
+        return fail(TG_ERR_ARG, "ldc=%lld < %lld", (long long)ldc, (long long)need_c);
+    if (M > 0 && N > 0) {
+        if (!C)
+            return fail(TG_ERR_NULL, "C is NULL");
+        if (K > 0 && !A)
+            return fail(TG_ERR_NULL, "A is NULL");
+        if (K > 0 && !B)
+            return fail(TG_ERR_NULL, "B is NULL");
+    }
+    return TG_OK;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static Problem make_problem(int64_t M, int64_t N, int64_t K, int dtype, int trans, int64_t lda,
+                            int64_t ldb, int64_t ldc, bool aligned)
+{
+    Problem p;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.dtype = dtype;
+    p.trans = trans;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.ptrs_aligned = aligned;
+    return p;
+}
+
+static Chip device_chip(const DeviceInfo &d)
+{
+    Chip c;
+    c.num_cus = d.cus;
+    return c;
+}
+
+// ---------------------------------------------------------------- execution
+
+static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const void *B, void *C,
+                    const tg_epilogue *epi, void *ws, hipStream_t s)
+{
+    const int epi_kind = epi ? (int)epi->kind : TG_EPI_NONE;
+    const float slope = epi ? epi->slope : 0.0f;
+    const int E = chunk_elems(p.dtype);
+    hipError_t e = hipSuccess;
+    if (pl.path == TG_PATH_NONE) {
+        if (p.M > 0 && p.N > 0)
+            e = launch_fill_zero(p.dtype, C, (int)p.M, (int)p.N, p.ldc, s);
+    } else if (pl.path == TG_PATH_MFMA) {
+        MfmaArgs a{};
+        a.A = A;
+        a.B = B;
+        a.C = C;
+        a.ws = (float *)ws;
+        a.lda = p.lda;
+        a.ldb = p.ldb;
+        a.ldc = p.ldc;
+        a.M = (int)p.M;
+        a.N = (int)p.N;
+        a.K = (int)p.K;
+        const int BK = pl.tile_k;
+        int64_t kps = (p.K + pl.split_k - 1) / pl.split_k;
+        kps = (kps + BK - 1) / BK * BK;
+        a.kps = (int)kps;
+        a.splits = pl.split_k;
+        a.tiles_m = (int)((p.M + pl.tile_m - 1) / pl.tile_m);
+        a.tiles_n = (int)((p.N + pl.tile_n - 1) / pl.tile_n);
+        a.epi = epi_kind;
+        a.slope = slope;
+        const int cb = elem_bytes(p.dtype);
+        a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
+        e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);
+        if (e == hipSuccess && pl.split_k > 1)
+            e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, (int)p.M, (int)p.N, C,
+                                     p.ldc, epi_kind, slope, a.c_vec, s);
+    } else if (pl.path == TG_PATH_GEMV) {
+        const bool ta = p.trans & TG_TRANS_A, tb = p.trans & TG_TRANS_B;
+        const bool rows_form = pl.tile_m == 4;
+        GemvArgs g{};
+        g.ws = (float *)ws;
+        g.K = (int)p.K;
+        g.epi = epi_kind;
+        g.slope = slope;
+        g.ksplit = pl.split_k;
+        g.O = C;
+        if (p.M == 1) {
+            // out(j) = C[j]; vector a(k) = A(0,k); matrix B
+            g.n = (int)p.N;
+            g.os = 1;
+            g.V = A;
+            g.vs = ta ? p.lda : 1;
+            g.X = B;
+            g.ldx = p.ldb;
+            (void)tb;
+        } else {
+            // N == 1: out(i) = C[i*ldc]; vector b(k) = B(k,0); matrix A
+            g.n = (int)p.M;
+            g.os = p.ldc;
+            g.V = B;
+            g.vs = tb ? 1 : p.ldb;
+            g.X = A;
+            g.ldx = p.lda;
+        }
+        if (!rows_form) {
+            int64_t rps = (p.K + pl.split_k - 1) / pl.split_k;
+            rps = (rps + 3) / 4 * 4;
+            g.rows_per_split = (int)rps;
+        } else {
+            g.rows_per_split = (int)p.K;
+        }
+        (void)E;
+        e = launch_gemv(p.dtype, rows_form, pl.vector_io != 0, g, s);
+    } else {
+        return fail(TG_ERR_UNSUPPORTED, "path %d has no kernel", pl.path);
+    }
+    if (e != hipSuccess)
+        return fail(TG_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    return TG_OK;
+}
+
+static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                     int64_t ldb, void *C, int64_t ldc, int dtype, int trans,
+                     const tg_epilogue *epi, const tg_options *opts, void *user_ws,
+                     size_t user_ws_bytes, void *stream)
+{
+    int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epi);
+    if (rc != TG_OK)
+        return rc;
+    if (M == 0 || N == 0)
+        return ok();
+    DeviceInfo *dev = nullptr;
+    rc = current_device(&dev);
+    if (rc != TG_OK)
+        return rc;
+    hipStream_t s = (hipStream_t)stream;
+    const bool aligned = aligned16(A) && aligned16(B);
+    Problem p = make_problem(M, N, K, dtype, trans, lda, ldb, ldc, aligned);
+    Chip chip = device_chip(*dev);
+    tg_plan pl;
+    const char *why = "";
+    rc = make_plan(p, chip, 0, opts, device_occ, dev, false, &pl, &why);
+    if (rc != TG_OK)
+        return fail(rc, "%s", why);
+
+    void *ws = nullptr;
+    bool own_ws = false;
+    if (pl.workspace_bytes > 0) {
+        if (user_ws) {
+            if (((uintptr_t)user_ws & 255u) != 0)
+                return fail(TG_ERR_ARG, "workspace must be 256-byte aligned");
+            if (user_ws_bytes >= pl.workspace_bytes) {
+                ws = user_ws;
+            }
+        } else {
+            hipError_t e = hipMallocAsync(&ws, pl.workspace_bytes, s);
+            if (e == hipSuccess)
+                own_ws = true;
+            else
+                ws = nullptr;
+        }
+        if (!ws) {
+            if (opts && opts->split_k > 1)
+                return fail(TG_ERR_ARG, "forced split_k=%d needs %llu bytes of workspace",
+                            opts->split_k, (unsigned long long)pl.workspace_bytes);
+            tg_options o = opts ? *opts : tg_options{TG_PATH_AUTO, 0, 0, 0};
+            o.split_k = 1;
+            rc = make_plan(p, chip, 0, &o, device_occ, dev, false, &pl, &why);
+            if (rc != TG_OK)
+                return fail(rc, "%s", why);
+        }
+    }
+    rc = run_plan(pl, p, A, B, C, epi, ws, s);
+    if (own_ws)
+        (void)hipFreeAsync(ws, s);
+    if (rc != TG_OK)
+        return rc;
+    return ok();
+}
+
+}  // namespace tg
+
+// ---------------------------------------------------------------- exported C ABI
+
+using namespace tg;
+
+extern "C" {
+
+int tg_gemm(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+            int64_t ldb, void *C, int64_t ldc, int dtype, int trans, const tg_epilogue *epilogue,
+            void *stream)
+{
+    return gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue, nullptr, nullptr, 0,
+                     stream);
+}
+
+int tg_gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+               int64_t ldb, void *C, int64_t ldc, int dtype, int trans,
+               const tg_epilogue *epilogue, const tg_options *opts, void *workspace,
+               size_t workspace_bytes, void *stream)
+{
+    return gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue, opts, workspace,
+                     workspace_bytes, stream);
+}
+
+int tg_gemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int trans, const tg_options *opts,
+                 tg_plan *out)
+{
+    if (!out)
+        return fail(TG_ERR_NULL, "out is NULL");
+    DeviceInfo *dev = nullptr;
+    int rc = current_device(&dev);
+    if (rc != TG_OK)
+        return rc;
+    const bool ta = trans & TG_TRANS_A, tb = trans & TG_TRANS_B;
+    Problem p = make_problem(M, N, K, dtype, trans, std::max<int64_t>(1, ta ? M : K),
+                             std::max<int64_t>(1, tb ? K : N), std::max<int64_t>(1, N), true);
+    const char *why = "";
+    rc = make_plan(p, device_chip(*dev), 0, opts, device_occ, dev, false, out, &why);
+    if (rc != TG_OK)
+        return fail(rc, "%s", why);
+    return ok();
+}
+
+int tg_plan_model(int64_t M, int64_t N, int64_t K, int dtype, int trans, int num_cus,
+                  int occupancy, const tg_options *opts, tg_plan *out)
+{
+    if (!out)
+        return fail(TG_ERR_NULL, "out is NULL");
+    const bool ta = trans & TG_TRANS_A, tb = trans & TG_TRANS_B;
+    Problem p = make_problem(M, N, K, dtype, trans, std::max<int64_t>(1, ta ? M : K),
+                             std::max<int64_t>(1, tb ? K : N), std::max<int64_t>(1, N), true);
+    Chip chip;
+    chip.num_cus = num_cus;
+    const char *why = "";
+    int rc = make_plan(p, chip, occupancy, opts, nullptr, nullptr, true, out, &why);
+    if (rc != TG_OK)
+        return fail(rc, "%s", why);
+    return ok();
+}
+
+size_t tg_workspace_size(int64_t M, int64_t N, int64_t K, int dtype, int trans,
+                         const tg_options *opts)
+{
+    tg_plan pl;
+    if (tg_gemm_plan(M, N, K, dtype, trans, opts, &pl) != TG_OK)
+        return 0;
+    return (size_t)pl.workspace_bytes;
+}
+
+int tg_device_cus(void)
+{
+    DeviceInfo *dev = nullptr;
+    int rc = current_device(&dev);
+    if (rc != TG_OK)
+        return rc;
+    return dev->cus;
+}
+
+const char *tg_last_error(void) { return g_err.c_str(); }
+
+int tg_version(void) { return TG_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,214 @@
+// gemv.hpp -- matrix-vector products (M == 1 or N == 1) on the vector ALUs.
+//
+// A product with M == 1 or N == 1 does about one multiply-add per matrix
+// element loaded, an arithmetic intensity below 1 FLOP/byte, so it is bound
+// by memory traffic on any GPU ("Matrix Multiplication Background User's
+// Guide", section 2).  These kernels use no matrix cores: they stream the
+// matrix once with coalesced 128-bit loads, multiply-add in float32 on the
+// vector ALUs and reduce across lanes, waves and K-splits.
+//
+// Two shapes cover every storage combination:
+//   cols: out(j) = sum_k v(k) * X[k][j]   X row-major K x n (contiguous along j)
+//   rows: out(i) = sum_k X[i][k] * v(k)   X row-major n x K (contiguous along k)
+// v(k) = V[k * vs] and out(j) = O[j * os] allow strided vectors.
+#pragma once
+
+#include "common.hpp"
+
+namespace tg {
+
+struct GemvArgs {
+    const void *X;
+    int64_t ldx;
+    const void *V;
+    int64_t vs;
+    void *O;
+    int64_t os;
+    float *ws;       // [ksplit][n] float32 partials when ksplit > 1
+    int n;           // output length
+    int K;
+    int ksplit;
+    int rows_per_split;
+    int epi;
+    float slope;
+};
+
+template <typename Tr>
+__device__ __forceinline__ float load_scalar(const void *p, int64_t i)
+{
+    return Tr::to_f32(((const typename Tr::T *)p)[i]);
+}
+
+// Unpack a 16-byte chunk into E floats.
+template <typename Tr>
+__device__ __forceinline__ void unpack(const u32x4 &c, float *f)
+{
+    if constexpr (Tr::kBytes == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            f[e] = __builtin_bit_cast(float, c[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t h = (uint16_t)chunk_elem<2>(c, e);
+            f[e] = Tr::to_f32(__builtin_bit_cast(typename Tr::T, h));
+        }
+    }
+}
+
+// cols form.  Grid: x = column strips of 64 chunks (64*E columns), y = K-splits.
+// The 4 waves of a workgroup take interleaved rows of the split's K range and
+// are summed in wave order through LDS.
+template <typename Tr, bool VEC>
+__global__ __launch_bounds__(256) void gemv_cols_kernel(GemvArgs p)
+{
+    using T = typename Tr::T;
+    constexpr int E = Tr::E;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = (blockIdx.x * 64 + lane) * E;
+    const int k_lo = blockIdx.y * p.rows_per_split;
+    const int k_hi = min(p.K, k_lo + p.rows_per_split);
+    const T *X = (const T *)p.X;
+
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        acc[e] = 0.f;
+
+    const bool col_in = col < p.n;
+    if (VEC && col_in) {
+        const T *base = X + col;
+        int k = k_lo + wave;
+        // 8 rows in flight per lane
+        for (; k + 28 < k_hi; k += 32) {
+            u32x4 x[8];
+            float a[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                x[u] = *(const u32x4 *)(base + (int64_t)(k + 4 * u) * p.ldx);
+                a[u] = load_scalar<Tr>(p.V, (int64_t)(k + 4 * u) * p.vs);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                float f[E];
+                unpack<Tr>(x[u], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    acc[e] += a[u] * f[e];
+            }
+        }
+        for (; k < k_hi; k += 4) {
+            const u32x4 x = *(const u32x4 *)(base + (int64_t)k * p.ldx);
+            const float a = load_scalar<Tr>(p.V, (int64_t)k * p.vs);
+            float f[E];
+            unpack<Tr>(x, f);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[e] += a * f[e];
+        }
+    } else if (col_in) {
+        for (int k = k_lo + wave; k < k_hi; k += 4) {
+            const float a = load_scalar<Tr>(p.V, (int64_t)k * p.vs);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (col + e < p.n)
+                    acc[e] += a * Tr::to_f32(X[(int64_t)k * p.ldx + col + e]);
+        }
+    }
+
+    // sum the 4 waves in order 0..3
+    __shared__ float red[4][64 * E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        red[wave][e * 64 + lane] = acc[e];
+    __syncthreads();
+    if (wave != 0 || !col_in)
+        return;
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        s[e] = ((red[0][e * 64 + lane] + red[1][e * 64 + lane]) + red[2][e * 64 + lane]) +
+               red[3][e * 64 + lane];
+    if (p.ksplit > 1) {
+        float *W = p.ws + (int64_t)blockIdx.y * p.n;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (col + e < p.n)
+                W[col + e] = s[e];
+    } else {
+        T *O = (T *)p.O;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (col + e < p.n)
+                O[(int64_t)(col + e) * p.os] = Tr::from_f32(apply_epi(s[e], p.epi, p.slope));
+    }
+}
+
+// out(j) = epi( sum_{z < ksplit} ws[z][j] ), increasing z.
+template <typename Tr>
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(GemvArgs p)
+{
+    using T = typename Tr::T;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= p.n)
+        return;
+    float s = 0.f;
+    for (int z = 0; z < p.ksplit; ++z)
+        s += p.ws[(int64_t)z * p.n + j];
+    ((T *)p.O)[(int64_t)j * p.os] = Tr::from_f32(apply_epi(s, p.epi, p.slope));
+}
+
+// rows form.  One wave per output: lanes stride over 16-byte chunks of the
+// row, then a butterfly reduction across the wave.  Grid: n / 4 workgroups.
+template <typename Tr, bool VEC>
+__global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs p)
+{
+    using T = typename Tr::T;
+    constexpr int E = Tr::E;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = blockIdx.x * 4 + wave;
+    if (i >= p.n)
+        return;
+    const T *row = (const T *)p.X + (int64_t)i * p.ldx;
+    const T *V = (const T *)p.V;
+    float acc = 0.f;
+    const int nchunks = VEC ? p.K / E : 0;
+    int c = lane;
+    for (; c + 192 < nchunks; c += 256) {
+        u32x4 x[4], v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            x[u] = *(const u32x4 *)(row + (int64_t)(c + 64 * u) * E);
+            v[u] = *(const u32x4 *)(V + (int64_t)(c + 64 * u) * E);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float fx[E], fv[E];
+            unpack<Tr>(x[u], fx);
+            unpack<Tr>(v[u], fv);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc += fx[e] * fv[e];
+        }
+    }
+    for (; c < nchunks; c += 64) {
+        const u32x4 x = *(const u32x4 *)(row + (int64_t)c * E);
+        const u32x4 v = *(const u32x4 *)(V + (int64_t)c * E);
+        float fx[E], fv[E];
+        unpack<Tr>(x, fx);
+        unpack<Tr>(v, fv);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            acc += fx[e] * fv[e];
+    }
+    // element-wise remainder (or the whole row without vector access)
+    for (int k = nchunks * E + lane; k < p.K; k += 64)
+        acc += Tr::to_f32(row[k]) * load_scalar<Tr>(p.V, (int64_t)k * p.vs);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        acc += __shfl_xor(acc, off, 64);
+    if (lane == 0)
+        ((T *)p.O)[(int64_t)i * p.os] = Tr::from_f32(apply_epi(acc, p.epi, p.slope));
+}
+
+}  // namespace tg

@@ -1,0 +1,6 @@
+// inst_bf16.hip -- kernel instances and launchers for bf16 storage.
+#include <algorithm>
+#define TG_TRAIT BF16
+#define TG_NAME bf16
+#define TG_TILE_LIST TG_TILE(256, 256) TG_TILE(256, 128) TG_TILE(128, 128) TG_TILE(128, 64) TG_TILE(64, 64)
+#include "instances.inc"

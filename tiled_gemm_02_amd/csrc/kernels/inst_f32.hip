@@ -1,0 +1,6 @@
+// inst_f32.hip -- kernel instances and launchers for f32 storage.
+#include <algorithm>
+#define TG_TRAIT F32
+#define TG_NAME f32
+#define TG_TILE_LIST TG_TILE(128, 128) TG_TILE(64, 64)
+#include "instances.inc"

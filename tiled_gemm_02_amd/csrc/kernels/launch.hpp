@@ -1,0 +1,38 @@
+// launch.hpp -- host-side launchers of the kernel instances (one translation
+// unit per storage type instantiates them).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemv.hpp"
+#include "mfma_gemm.hpp"
+
+namespace tg {
+
+// hipErrorInvalidValue: no instance for this (type, tile, load width).
+hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, const MfmaArgs &a,
+                       hipStream_t s);
+// Resident workgroups per CU of an instance (0 if none).
+int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec);
+hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, int N, void *C,
+                                int64_t ldc, int epi, float slope, int c_vec, hipStream_t s);
+hipError_t launch_fill_zero(int dtype, void *C, int M, int N, int64_t ldc, hipStream_t s);
+// rows_form: outputs are contiguous dot products; else column streaming.
+hipError_t launch_gemv(int dtype, bool rows_form, bool vec, const GemvArgs &a, hipStream_t s);
+
+#define TG_DECLARE_TYPE_LAUNCHERS(NAME)                                                          \
+    hipError_t launch_mfma_##NAME(int trans, int bm, int bn, bool vec, const MfmaArgs &a,        \
+                                  hipStream_t s);                                                \
+    int mfma_occupancy_##NAME(int trans, int bm, int bn, bool vec);                              \
+    hipError_t launch_splitk_reduce_##NAME(const float *ws, int splits, int M, int N, void *C,   \
+                                           int64_t ldc, int epi, float slope, int c_vec,         \
+                                           hipStream_t s);                                       \
+    hipError_t launch_fill_zero_##NAME(void *C, int M, int N, int64_t ldc, hipStream_t s);       \
+    hipError_t launch_gemv_##NAME(bool rows_form, bool vec, const GemvArgs &a, hipStream_t s);
+
+TG_DECLARE_TYPE_LAUNCHERS(f16)
+TG_DECLARE_TYPE_LAUNCHERS(bf16)
+TG_DECLARE_TYPE_LAUNCHERS(f32)
+
+}  // namespace tg

@@ -1,0 +1,419 @@
+// plan.cpp -- the planner: which kernel, which tile, how many K-splits.
+//
+// The model follows "Matrix Multiplication Background User's Guide":
+//   * section 2: arithmetic intensity 2MNK / (bytes of A, B, C) against the
+//     chip's FLOP:byte ratio separates memory-bound calls (GEMV when M or N
+//     is 1, the skinny kernel when one output dimension is small) from
+//     math-bound ones;
+//   * section 2.3: larger tiles reuse more data and run more efficiently,
+//     smaller tiles give more parallel work; K may be split when M and N are
+//     small and K large, at the price of a final reduction;
+//   * section 3.1 (tile quantization): ceil(M/Mt) * ceil(N/Nt) tiles each do
+//     a full tile of math, however little of it is useful;
+//   * section 3.2 (wave quantization): tiles run in waves of
+//     (compute units x tiles resident per unit); a partial last wave costs
+//     about as much as a full one.
+// Every candidate (tile, split) is priced as waves x time-per-wave, floored by
+// the HBM time of the algorithmic bytes; ties (within 3%) go to the larger
+// tile, then to fewer tiles, then to fewer splits.
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace tg {
+
+// Relative per-CU efficiencies are measured values of these kernels on
+// MI355X (largest tile = 1); LDS is 2 stages x (BM + BN) rows x 128 bytes.
+static const TileSpec kTiles16[] = {
+    {256, 256, 1.00, 128}, {256, 128, 0.90, 96}, {128, 128, 0.78, 64},
+    {128, 64, 0.60, 48},   {64, 64, 0.42, 32},
+};
+static const TileSpec kTiles32[] = {
+    {128, 128, 1.00, 64},
+    {64, 64, 0.60, 32},
+};
+
+int tile_menu(int dtype, const TileSpec **out)
+{
+    if (dtype == TG_F32) {
+        *out = kTiles32;
+        return (int)(sizeof kTiles32 / sizeof kTiles32[0]);
+    }
+    *out = kTiles16;
+    return (int)(sizeof kTiles16 / sizeof kTiles16[0]);
+}
+
+bool has_mfma_tile(int dtype, int bm, int bn, bool vec)
+{
+    if (!vec)
+        return bm == 64 && bn == 64;
+    const TileSpec *t;
+    int n = tile_menu(dtype, &t);
+    for (int i = 0; i < n; ++i)
+        if (t[i].bm == bm && t[i].bn == bn)
+            return true;
+    return false;
+}
+
+static const TileSpec *find_tile(int dtype, int bm, int bn)
+{
+    const TileSpec *t;
+    int n = tile_menu(dtype, &t);
+    for (int i = 0; i < n; ++i)
+        if (t[i].bm == bm && t[i].bn == bn)
+            return &t[i];
+    return nullptr;
+}
+
+int model_occupancy(int dtype, int bm, int bn, bool vec)
+{
+    (void)vec;
+    const int lds_kib = 2 * (bm + bn) * 128 / 1024;
+    int by_lds = 160 / std::max(1, lds_kib);
+    // register-limited residency (waves per SIMD) of each tile's wave sub-tile
+    int by_regs;
+    const int area = bm * bn;
+    if (area >= 256 * 256)
+        by_regs = 1;
+    else if (area >= 256 * 128)
+        by_regs = dtype == TG_F32 ? 2 : 1;
+    else if (area >= 128 * 128)
+        by_regs = 2;
+    else if (area >= 128 * 64)
+        by_regs = 3;
+    else
+        by_regs = 4;
+    return std::max(1, std::min(by_lds, by_regs));
+}
+
+static double flop_rate_cu(const Chip &c, int dtype)
+{
+    const double per_clk = dtype == TG_F32 ? c.mfma32_flop_clk : c.mfma16_flop_clk;
+    return per_clk * c.clock_ghz * 1e9;
+}
+
+static double chip_peak(const Chip &c, int dtype) { return flop_rate_cu(c, dtype) * c.num_cus; }
+
+static double alg_bytes(const Problem &p)
+{
+    const double s = elem_bytes(p.dtype);
+    return s * ((double)p.M * p.K + (double)p.K * p.N + (double)p.M * p.N);
+}
+
+static void fill_common(const Problem &p, const Chip &chip, tg_plan *out)
+{
+    out->num_cus = chip.num_cus;
+    const double bytes = alg_bytes(p);
+    out->arith_intensity = bytes > 0 ? 2.0 * p.M * p.N * p.K / bytes : 0.0;
+}
+
+static bool vec_ok(const Problem &p)
+{
+    const int E = chunk_elems(p.dtype);
+    return p.ptrs_aligned && p.M % E == 0 && p.N % E == 0 && p.K % E == 0 && p.lda % E == 0 &&
+           p.ldb % E == 0;
+}
+
+// ---------------------------------------------------------------- GEMV
+
+static int plan_gemv(const Problem &p, const Chip &chip, const tg_options *opts, tg_plan *out,
+                     const char **why)
+{
+    (void)opts;
+    if (!(p.M == 1 || p.N == 1)) {
+        *why = "GEMV path needs M == 1 or N == 1";
+        return TG_ERR_UNSUPPORTED;
+    }
+    const int E = chunk_elems(p.dtype);
+    const bool ta = p.trans & TG_TRANS_A, tb = p.trans & TG_TRANS_B;
+    // rows form: output elements are contiguous dot products
+    const bool rows_form = (p.M == 1) ? tb : !ta;
+    const int64_t n = (p.M == 1) ? p.N : p.M;
+    out->path = TG_PATH_GEMV;
+    out->tile_k = 0;
+    out->occupancy = 8;
+    if (rows_form) {
+        out->tile_m = 4;   // outputs per workgroup (one per wave)
+        out->tile_n = 1;
+        out->split_k = 1;
+        out->tiles = (n + 3) / 4;
+        out->workgroups = out->tiles;
+        out->workspace_bytes = 0;
+        // vector loads need a unit-stride, aligned vector and aligned rows
+        const int64_t vs = (p.M == 1) ? (ta ? p.lda : 1) : (tb ? 1 : p.ldb);
+        const int64_t ldx = (p.M == 1) ? p.ldb : p.lda;
+        out->vector_io = p.ptrs_aligned && vs == 1 && ldx % E == 0 && p.K % E == 0;
+    } else {
+        const int64_t cols_per_wg = 64LL * E;
+        const int64_t strips = (n + cols_per_wg - 1) / cols_per_wg;
+        // enough workgroups to keep every CU streaming: about 8 per CU
+        const int64_t want = 8LL * chip.num_cus;
+        int64_t ks = std::max<int64_t>(1, (want + strips - 1) / strips);
+        ks = std::min<int64_t>(ks, std::max<int64_t>(1, p.K / 32));
+        if (opts && opts->split_k > 0)
+            ks = std::min<int64_t>(opts->split_k, std::max<int64_t>(1, p.K));
+        int64_t rps = (p.K + ks - 1) / ks;
+        rps = (rps + 3) / 4 * 4;
+        ks = (p.K + rps - 1) / rps;
+        out->tile_m = 1;
+        out->tile_n = (int)cols_per_wg;
+        out->split_k = (int)ks;
+        out->tiles = strips;
+        out->workgroups = strips * ks;
+        out->workspace_bytes = ks > 1 ? (uint64_t)ks * (uint64_t)n * 4u : 0;
+        const int64_t ldx = (p.M == 1) ? p.ldb : p.lda;
+        out->vector_io = p.ptrs_aligned && n % E == 0 && ldx % E == 0;
+    }
+    const int64_t slots = (int64_t)chip.num_cus * out->occupancy;
+    out->waves = (out->workgroups + slots - 1) / slots;
+    out->tile_eff = 1.0;
+    out->wave_eff = (double)out->workgroups / (double)(out->waves * slots);
+    const double bytes = alg_bytes(p) + (double)out->workspace_bytes * 2;
+    out->pred_us = bytes / (chip.hbm_gbs * 1e3) + (out->split_k > 1 ? chip.launch_us : 0.0);
+    out->pred_eff = (2.0 * p.M * p.N * p.K / (out->pred_us * 1e-6)) / chip_peak(chip, p.dtype);
+    return TG_OK;
+}
+
+// ---------------------------------------------------------------- macro tiles
+
+struct Cand {
+    int bm, bn, s, occ, kps;
+    int64_t tiles, units, waves;
+    double t, eff;
+};
+
+static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int occ, double eff)
+{
+    Cand c{};
+    const int BK = 8 * chunk_elems(p.dtype);
+    c.bm = bm;
+    c.bn = bn;
+    c.occ = occ;
+    c.eff = eff;
+    int64_t kps = (p.K + s - 1) / s;
+    kps = (kps + BK - 1) / BK * BK;
+    c.kps = (int)kps;
+    c.s = (int)((p.K + kps - 1) / kps);
+    c.tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+    c.units = c.tiles * c.s;
+    const int64_t slots = (int64_t)chip.num_cus * occ;
+    c.waves = (c.units + slots - 1) / slots;
+    const double t_unit = occ * (2.0 * bm * bn * (double)kps) / (flop_rate_cu(chip, p.dtype) * eff);
+    double t = c.waves * t_unit;
+    double bytes = alg_bytes(p);
+    if (c.s > 1)
+        bytes += 2.0 * c.s * (double)p.M * p.N * 4.0;
+    t = std::max(t, bytes / (chip.hbm_gbs * 1e9));
+    if (c.s > 1)
+        t += chip.launch_us * 1e-6;
+    c.t = t;
+    return c;
+}
+
+static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg_options *opts,
+                     OccFn occ_fn, void *occ_ctx, bool model, tg_plan *out, const char **why)
+{
+    const bool vec = vec_ok(p);
+    const int E = chunk_elems(p.dtype);
+    const int BK = 8 * E;
+    const TileSpec generic = {64, 64, 0.42, 32};
+    const TileSpec *menu;
+    int nmenu;
+    if (vec) {
+        nmenu = tile_menu(p.dtype, &menu);
+    } else {
+        menu = &generic;
+        nmenu = 1;
+    }
+    // forced tile
+    TileSpec forced{};
+    if (opts && (opts->tile_m > 0 || opts->tile_n > 0)) {
+        if (opts->tile_m <= 0 || opts->tile_n <= 0) {
+            *why = "a forced tile needs both tile_m and tile_n";
+            return TG_ERR_ARG;
+        }
+        const TileSpec *f = vec ? find_tile(p.dtype, opts->tile_m, opts->tile_n) : nullptr;
+        if (!vec && opts->tile_m == 64 && opts->tile_n == 64)
+            f = &generic;
+        if (!f) {
+            if (!model) {
+                *why = "no macro-tile kernel of the forced size for these operands";
+                return TG_ERR_UNSUPPORTED;
+            }
+            // the model prices any tile (e.g. another chip's tile menu)
+            forced = TileSpec{opts->tile_m, opts->tile_n, 1.0, 0};
+            f = &forced;
+        }
+        menu = f;
+        nmenu = 1;
+    }
+    int splits[16];
+    int nsplit = 0;
+    if (opts && opts->split_k > 0) {
+        splits[nsplit++] = opts->split_k;
+    } else {
+        const int cand[] = {1, 2, 3, 4, 6, 8, 12, 16};
+        for (int s : cand)
+            if (s == 1 || (int64_t)s * 2 * BK <= p.K)
+                splits[nsplit++] = s;
+    }
+    bool have = false;
+    Cand best{};
+    for (int i = 0; i < nmenu; ++i) {
+        const TileSpec &ts = menu[i];
+        int occ = occupancy > 0 ? occupancy
+                                : (occ_fn ? occ_fn(p.dtype, p.trans, ts.bm, ts.bn, vec, occ_ctx)
+                                          : model_occupancy(p.dtype, ts.bm, ts.bn, vec));
+        occ = std::max(1, occ);
+        for (int j = 0; j < nsplit; ++j) {
+            Cand c = price(p, chip, ts.bm, ts.bn, splits[j], occ, ts.eff);
+            if (!have) {
+                best = c;
+                have = true;
+                continue;
+            }
+            const double tol = 0.03;
+            if (c.t < best.t * (1 - tol)) {
+                best = c;
+            } else if (c.t <= best.t * (1 + tol)) {
+                // near-tie: larger tile, then fewer tiles, then fewer splits
+                const int64_t ac = (int64_t)c.bm * c.bn, ab = (int64_t)best.bm * best.bn;
+                if (ac > ab || (ac == ab && (c.tiles < best.tiles ||
+                                             (c.tiles == best.tiles && c.s < best.s))))
+                    best = c;
+            }
+        }
+    }
+    out->path = TG_PATH_MFMA;
+    out->tile_m = best.bm;
+    out->tile_n = best.bn;
+    out->tile_k = BK;
+    out->split_k = best.s;
+    out->occupancy = best.occ;
+    out->vector_io = vec ? 1 : 0;
+    out->tiles = best.tiles;
+    out->workgroups = best.units;
+    out->waves = best.waves;
+    out->tile_eff = (double)p.M * p.N / ((double)best.tiles * best.bm * best.bn);
+    out->wave_eff = (double)best.units / ((double)best.waves * chip.num_cus * best.occ);
+    out->pred_us = best.t * 1e6;
+    out->pred_eff = (2.0 * p.M * p.N * p.K / best.t) / chip_peak(chip, p.dtype);
+    out->workspace_bytes = best.s > 1 ? (uint64_t)best.s * p.M * p.N * 4u : 0;
+    return TG_OK;
+}
+
+// ---------------------------------------------------------------- skinny
+
+static bool skinny_fits(const Problem &p)
+{
+    return p.dtype != TG_F32 && p.N <= kSkinnyMaxN && p.N >= 2 && p.M >= 2 * kSkinnyRows &&
+           vec_ok(p) && !(p.trans & TG_TRANS_A) && !(p.trans & TG_TRANS_B);
+}
+
+static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opts, tg_plan *out,
+                       const char **why)
+{
+    if (!kSkinnyEnabled) {
+        *why = "skinny kernel not built";
+        return TG_ERR_UNSUPPORTED;
+    }
+    if (!skinny_fits(p)) {
+        *why = "skinny path needs 16-bit NN operands, 2 <= N <= 128, M >= 128, 16-byte aligned";
+        return TG_ERR_UNSUPPORTED;
+    }
+    const int BK = 64;
+    const int64_t tm = (p.M + kSkinnyRows - 1) / kSkinnyRows;
+    // split K until the grid covers every CU about twice, one BK step per split at least
+    int s = 1;
+    if (opts && opts->split_k > 0) {
+        s = opts->split_k;
+    } else {
+        while (tm * s < 2LL * chip.num_cus && (int64_t)(s * 2) * 4 * BK <= p.K && s < 16)
+            s *= 2;
+    }
+    int64_t kps = (p.K + s - 1) / s;
+    kps = (kps + BK - 1) / BK * BK;
+    s = (int)((p.K + kps - 1) / kps);
+    out->path = TG_PATH_SKINNY;
+    out->tile_m = kSkinnyRows;
+    out->tile_n = kSkinnyMaxN;
+    out->tile_k = BK;
+    out->split_k = s;
+    out->occupancy = 2;
+    out->vector_io = 1;
+    out->tiles = tm;
+    out->workgroups = tm * s;
+    const int64_t slots = (int64_t)chip.num_cus * out->occupancy;
+    out->waves = (out->workgroups + slots - 1) / slots;
+    out->tile_eff = (double)p.N / kSkinnyMaxN * (double)p.M / (tm * kSkinnyRows);
+    out->wave_eff = (double)out->workgroups / (double)(out->waves * slots);
+    out->workspace_bytes = s > 1 ? (uint64_t)s * p.M * p.N * 4u : 0;
+    const double bytes = alg_bytes(p) + 2.0 * (double)out->workspace_bytes;
+    out->pred_us = bytes / (chip.hbm_gbs * 1e3) + (s > 1 ? chip.launch_us : 0.0);
+    out->pred_eff = (2.0 * p.M * p.N * p.K / (out->pred_us * 1e-6)) / chip_peak(chip, p.dtype);
+    return TG_OK;
+}
+
+// ---------------------------------------------------------------- entry
+
+int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_options *opts,
+              OccFn occ, void *occ_ctx, bool model, tg_plan *out, const char **why)
+{
+    static const char *none = "";
+    *why = none;
+    *out = tg_plan{};
+    if (p.M < 0 || p.N < 0 || p.K < 0) {
+        *why = "negative dimension";
+        return TG_ERR_ARG;
+    }
+    if (p.dtype < TG_F32 || p.dtype > TG_BF16) {
+        *why = "unknown dtype";
+        return TG_ERR_ARG;
+    }
+    if (p.trans < 0 || p.trans > 3) {
+        *why = "unknown trans";
+        return TG_ERR_ARG;
+    }
+    if (chip.num_cus <= 0) {
+        *why = "num_cus must be positive";
+        return TG_ERR_ARG;
+    }
+    fill_common(p, chip, out);
+    out->split_k = 1;
+    if (p.M == 0 || p.N == 0 || p.K == 0) {
+        out->path = TG_PATH_NONE;
+        out->pred_us = 0.0;
+        return TG_OK;
+    }
+    int path = opts ? opts->path : TG_PATH_AUTO;
+    if (path == TG_PATH_AUTO) {
+        const double ridge = chip_peak(chip, p.dtype) / (chip.hbm_gbs * 1e9);
+        if (p.M == 1 || p.N == 1)
+            path = TG_PATH_GEMV;
+        else if (kSkinnyEnabled && skinny_fits(p) && out->arith_intensity < ridge)
+            path = TG_PATH_SKINNY;
+        else
+            path = TG_PATH_MFMA;
+    }
+    int rc;
+    switch (path) {
+    case TG_PATH_MFMA:
+        rc = plan_mfma(p, chip, occupancy, opts, occ, occ_ctx, model, out, why);
+        break;
+    case TG_PATH_GEMV:
+        rc = plan_gemv(p, chip, opts, out, why);
+        break;
+    case TG_PATH_SKINNY:
+        rc = plan_skinny(p, chip, opts, out, why);
+        break;
+    default:
+        *why = "unknown forced path";
+        rc = TG_ERR_ARG;
+    }
+    if (rc == TG_OK)
+        fill_common(p, chip, out);
+    return rc;
+}
+
+}  // namespace tg

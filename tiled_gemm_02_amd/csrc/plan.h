@@ -1,0 +1,68 @@
+// plan.h -- host-side planner: path choice, tile choice, split-K, and the
+// tile/wave quantization model behind them.  Pure C++ (no HIP), so the model
+// can be exercised on a machine without a GPU.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/tg_gemm.h"
+
+namespace tg {
+
+// Chip description the model plans against.
+struct Chip {
+    int num_cus = 256;            // MI355X: 8 XCDs x 32 CUs
+    double clock_ghz = 2.4;       // peak engine clock
+    double mfma16_flop_clk = 4096;  // dense fp16/bf16 matrix-core FLOP per clock per CU
+    double mfma32_flop_clk = 256;   // fp32 matrix-core FLOP per clock per CU
+    double valu_flop_clk = 256;     // fp32 vector FMA FLOP per clock per CU
+    double hbm_gbs = 8000.0;      // HBM3E bandwidth, GB/s
+    double launch_us = 2.0;       // cost charged per extra kernel launch
+};
+
+// Everything the planner may look at for one call.
+struct Problem {
+    int64_t M, N, K;
+    int dtype;       // tg_dtype
+    int trans;       // tg_trans
+    int64_t lda, ldb, ldc;
+    bool ptrs_aligned;  // A, B (and C) 16-byte aligned
+};
+
+// Macro-tile kernels compiled into the library (tile_m x tile_n), per
+// storage type, with their per-CU efficiency relative to the largest tile
+// and the LDS each workgroup holds.  Element-wise ("generic") loads exist for
+// one tile only.
+struct TileSpec {
+    int bm, bn;
+    double eff;      // relative throughput of a saturated CU
+    int lds_kib;     // LDS per workgroup (2 stages)
+};
+
+int tile_menu(int dtype, const TileSpec **out);       // vector-load tiles, largest first
+bool has_mfma_tile(int dtype, int bm, int bn, bool vec);
+
+// Residency of a tile kernel on one CU when no measured value is given:
+// limited by LDS (160 KiB per CU) and the kernels' register use.
+int model_occupancy(int dtype, int bm, int bn, bool vec);
+
+// Skinny kernel geometry (N <= kSkinnyMaxN).
+constexpr int kSkinnyRows = 64;    // output rows per workgroup
+constexpr int kSkinnyMaxN = 128;   // widest output it covers in one pass
+constexpr bool kSkinnyEnabled = false;
+
+// Occupancy lookup: returns workgroups per CU for a tile kernel; the device
+// path fills this from the runtime, the model from model_occupancy().
+typedef int (*OccFn)(int dtype, int trans, int bm, int bn, bool vec, void *ctx);
+
+// Plan one call.  occupancy > 0 forces that residency for every kernel.
+// Returns TG_OK or a tg_status; `why` receives a static description on error.
+// model: called from the pure model, which may price tiles no kernel offers.
+int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_options *opts,
+              OccFn occ, void *occ_ctx, bool model, tg_plan *out, const char **why);
+
+// 16-byte-chunk element count of a storage type.
+inline int chunk_elems(int dtype) { return dtype == TG_F32 ? 4 : 8; }
+inline int elem_bytes(int dtype) { return dtype == TG_F32 ? 4 : 2; }
+
+}  // namespace tg
