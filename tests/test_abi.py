@@ -1,0 +1,86 @@
+"""The C-ABI library: loads, exports every declared symbol, validates arguments
+and reports a missing GPU, all without launching anything (CPU only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_gemm_02_amd as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "tg_gemm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    for must in ("tg_gemm", "tg_gemm_ex", "tg_gemm_plan", "tg_plan_model", "tg_workspace_size",
+                 "tg_device_cus", "tg_last_error", "tg_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tg.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} declared in tg_gemm.h but not exported"
+
+
+def test_version():
+    assert tg.tg_version() == 100
+
+
+def test_argument_errors():
+    F16 = tg.TG_F16
+    # unknown enums
+    assert tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, 7, 0) == tg.TG_ERR_ARG
+    assert tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, F16, 9) == tg.TG_ERR_ARG
+    assert tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, F16, 0, (5, 0.1)) == tg.TG_ERR_ARG
+    # negative sizes and short leading dimensions
+    assert tg.tg_gemm(-1, 4, 4, 1, 4, 1, 4, 1, 4, F16, 0) == tg.TG_ERR_ARG
+    assert tg.tg_gemm(4, 4, 4, 1, 3, 1, 4, 1, 4, F16, 0) == tg.TG_ERR_ARG
+    assert "lda" in tg.tg_last_error()
+    assert tg.tg_gemm(4, 4, 8, 1, 8, 1, 3, 1, 4, F16, 0) == tg.TG_ERR_ARG
+    assert tg.tg_gemm(4, 4, 8, 1, 8, 1, 4, 1, 3, F16, 0) == tg.TG_ERR_ARG
+    # transposed operands need ld >= M (A) and >= K (B)
+    assert tg.tg_gemm(6, 4, 8, 1, 5, 1, 8, 1, 4, F16, tg.TG_TT) == tg.TG_ERR_ARG
+    assert tg.tg_gemm(6, 4, 8, 1, 6, 1, 7, 1, 4, F16, tg.TG_TT) == tg.TG_ERR_ARG
+    # NULL operands with elements
+    assert tg.tg_gemm(4, 4, 4, None, 4, 1, 4, 1, 4, F16, 0) == tg.TG_ERR_NULL
+    assert tg.tg_gemm(4, 4, 4, 1, 4, None, 4, 1, 4, F16, 0) == tg.TG_ERR_NULL
+    assert tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, None, 4, F16, 0) == tg.TG_ERR_NULL
+
+
+def test_quick_returns_need_no_device():
+    # M == 0 or N == 0: nothing to do, valid even with NULL operands
+    assert tg.tg_gemm(0, 4, 4, None, 4, None, 4, None, 4, tg.TG_F16, 0) == tg.TG_OK
+    assert tg.tg_gemm(4, 0, 4, None, 4, None, 1, None, 1, tg.TG_F16, 0) == tg.TG_OK
+    assert tg.tg_last_error() == ""
+
+
+def test_no_device_is_reported():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    rc = tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, tg.TG_F16, 0)
+    assert rc == tg.TG_ERR_DEVICE
+    assert tg.tg_device_cus() == tg.TG_ERR_DEVICE
+    with pytest.raises(tg.TgError):
+        tg.tg_gemm_plan(64, 64, 64, tg.TG_F16)
+
+
+def test_plan_model_rejects_bad_input():
+    with pytest.raises(tg.TgError):
+        tg.tg_plan_model(4, 4, 4, 9)
+    with pytest.raises(tg.TgError):
+        tg.tg_plan_model(4, 4, 4, tg.TG_F16, num_cus=0)
+    with pytest.raises(tg.TgError):
+        tg.tg_plan_model(4, 4, 4, tg.TG_F16, options=dict(path=tg.TG_PATH_GEMV))
+    with pytest.raises(tg.TgError):
+        tg.tg_plan_model(4, 4, 4, tg.TG_F16, options=dict(tile_m=64))

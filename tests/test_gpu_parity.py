@@ -1,0 +1,278 @@
+"""GPU parity: the HIP library against the float64 oracle (run with -m gpu).
+
+Tolerance (from the oracle): |C - C_ref| <= 1e-4 (|A||B|)_ij + 1e-6 + r_out |C_ref|,
+r_out = 0 (f32), 1e-3 (f16), 2^-8 (bf16).  Integer-valued operands whose
+partial sums are exact in float32 must match bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gemm_inputs import (BF16, F16, F32, NN, NT, TN, TT, WORKLOADS, make_int_problem, make_problem,
+                         layout, round_to)
+from tests.gpu_helpers import check_full, check_sampled, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [F32, F16, BF16]
+TRANS = [NN, TN, NT, TT]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    import tiled_gemm_02_amd as tg
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tg.load()
+    _say("device", torch.cuda.get_device_name(0), "cus", tg.tg_device_cus())
+    yield
+
+
+# ---------------------------------------------------------------- small shapes, full compare
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans", TRANS)
+@pytest.mark.parametrize("shape", [(64, 64, 64), (128, 96, 200), (200, 136, 72), (264, 520, 136)])
+def test_aligned_shapes(dtype, trans, shape):
+    M, N, K = shape
+    _say("case", dtype, trans, shape)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=3)
+    r, _, _ = check_full(p)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans", TRANS)
+@pytest.mark.parametrize("shape", [(1, 7, 31), (7, 1, 33), (33, 31, 7), (31, 33, 1), (255, 257, 33),
+                                   (257, 255, 31), (65, 130, 257)])
+def test_ragged_shapes(dtype, trans, shape):
+    M, N, K = shape
+    _say("case", dtype, trans, shape)
+    p = make_problem(M, N, K, dtype, trans, "normal", seed=5)
+    r, _, _ = check_full(p)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans", TRANS)
+def test_padded_leading_dims(dtype, trans):
+    _say("case ld_pad", dtype, trans)
+    p = make_problem(136, 72, 96, dtype, trans, "uniform", seed=1, ld_pad=8)
+    r, _, _ = check_full(p, out_pad=8)
+    assert r["ok"], r
+    p = make_problem(100, 60, 90, dtype, trans, "uniform", seed=1, ld_pad=3)
+    r, _, _ = check_full(p, out_pad=5)
+    assert r["ok"], r
+
+
+# ---------------------------------------------------------------- exactness pins on the GPU
+
+@pytest.mark.parametrize("trans", TRANS)
+@pytest.mark.parametrize("dtype,lo,hi,K", [(F16, -2, 2, 512), (BF16, -1, 1, 256), (F32, -4, 4, 1024)])
+def test_integer_products_bitwise(trans, dtype, lo, hi, K):
+    _say("case int", dtype, trans, K)
+    p = make_int_problem(136, 200, K, dtype, trans, lo, hi, seed=2)
+    r, got, ref = check_full(p)
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_identity_and_permutation_bitwise(dtype):
+    rng = np.random.default_rng(0)
+    M, K = 96, 128
+    A = round_to(rng.uniform(-1, 1, (M, K)), dtype)
+    from gemm_inputs import Problem, stored_to_f64
+    A64 = stored_to_f64(A, dtype)
+    I = round_to(np.eye(K), dtype)
+    p = Problem(M, K, K, dtype, NN, A, I, K, K)
+    got = run_gpu(p)
+    np.testing.assert_array_equal(got, A64)
+    perm = rng.permutation(K)
+    P = np.zeros((K, K))
+    P[perm, np.arange(K)] = 1.0
+    p = Problem(M, K, K, dtype, NN, A, round_to(P, dtype), K, K)
+    got = run_gpu(p)
+    np.testing.assert_array_equal(got, A64[:, perm])
+
+
+# ---------------------------------------------------------------- degenerate and edge cases
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_k_zero_writes_zero(dtype):
+    import torch
+    import tiled_gemm_02_amd as tg
+    from tests.gpu_helpers import torch_dtype
+    A = torch.empty((5, 0), dtype=torch_dtype(dtype), device="cuda:0")
+    B = torch.empty((0, 7), dtype=torch_dtype(dtype), device="cuda:0")
+    C = torch.full((5, 7), 3.0, dtype=torch_dtype(dtype), device="cuda:0")
+    tg.gemm(A, B, out=C, epilogue=(tg.TG_EPI_LEAKY_RELU, 0.01))
+    torch.cuda.synchronize()
+    assert torch.all(C == 0)
+
+
+def test_empty_outputs_are_noops():
+    import torch
+    import tiled_gemm_02_amd as tg
+    A = torch.ones((0, 8), dtype=torch.float16, device="cuda:0")
+    B = torch.ones((8, 4), dtype=torch.float16, device="cuda:0")
+    C = tg.gemm(A, B)
+    assert C.shape == (0, 4)
+    assert tg.tg_gemm(4, 0, 8, 1, 8, 1, 0 + 1, 1, 1, tg.TG_F16, 0) == tg.TG_OK
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans", TRANS)
+def test_leaky_relu_epilogue(dtype, trans):
+    _say("case leaky", dtype, trans)
+    p = make_problem(200, 264, 128, dtype, trans, "normal", seed=4)
+    r, got, ref = check_full(p, epilogue="leaky_relu", slope=0.01)
+    assert r["ok"], r
+    assert (ref < 0).any() and (ref > 0).any()
+
+
+# ---------------------------------------------------------------- forced plans
+
+def _tiles(dtype):
+    return [(128, 128), (64, 64)] if dtype == F32 else [(256, 256), (256, 128), (128, 128), (128, 64), (64, 64)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans", [NN, NT])
+def test_every_tile(dtype, trans):
+    for tm, tn in _tiles(dtype):
+        _say("case tile", dtype, trans, tm, tn)
+        p = make_problem(296, 280, 136, dtype, trans, "normal", seed=6)
+        r, _, _ = check_full(p, options=dict(tile_m=tm, tile_n=tn, split_k=1))
+        assert r["ok"], (tm, tn, r)
+    # element-wise loads exist for 64 x 64 only; other forced tiles are refused
+    import tiled_gemm_02_amd as tg
+    p = make_problem(300, 281, 137, dtype, trans, "normal", seed=6)
+    r, _, _ = check_full(p, options=dict(tile_m=64, tile_n=64, split_k=1))
+    assert r["ok"], r
+    with pytest.raises(tg.TgError):
+        run_gpu(p, options=dict(tile_m=128, tile_n=128))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("split", [2, 3, 5])
+def test_split_k(dtype, split):
+    _say("case split", dtype, split)
+    p = make_problem(136, 96, 1000 if dtype != F32 else 1000, dtype, NN, "normal", seed=7)
+    for epi in (None, "leaky_relu"):
+        r, _, _ = check_full(p, epilogue=epi, options=dict(split_k=split))
+        assert r["ok"], (split, epi, r)
+
+
+def test_split_k_caller_workspace():
+    import torch
+    import tiled_gemm_02_amd as tg
+    p = make_problem(128, 128, 2048, F16, NN, "normal", seed=8)
+    need = tg.tg_workspace_size(128, 128, 2048, F16, NN, dict(split_k=4))
+    assert need == 4 * 128 * 128 * 4
+    ws = torch.empty(need // 4, dtype=torch.float32, device="cuda:0")
+    r, _, _ = check_full(p, options=dict(split_k=4), workspace=ws)
+    assert r["ok"], r
+    small = torch.empty(16, dtype=torch.float32, device="cuda:0")
+    with pytest.raises(tg.TgError):
+        run_gpu(p, options=dict(split_k=4), workspace=small)
+    r, _, _ = check_full(p, workspace=small)  # planner's choice falls back to no split
+    assert r["ok"], r
+
+
+# ---------------------------------------------------------------- skinny path
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("trans", [NN, NT])
+@pytest.mark.parametrize("shape", [(128, 128, 256), (200, 64, 264), (1000, 120, 1000), (136, 8, 512),
+                                   (4096, 128, 2048)])
+def test_skinny(dtype, trans, shape):
+    import tiled_gemm_02_amd as tg
+    M, N, K = shape
+    _say("case skinny", dtype, trans, shape)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=11)
+    opts = dict(path=tg.TG_PATH_SKINNY)
+    assert tg.tg_gemm_plan(M, N, K, dtype, trans, opts)["path"] == tg.TG_PATH_SKINNY
+    r, _, _ = check_full(p, options=opts)
+    assert r["ok"], r
+    for split in (1, 3):
+        r, _, _ = check_full(p, epilogue="leaky_relu", options=dict(path=tg.TG_PATH_SKINNY, split_k=split))
+        assert r["ok"], (split, r)
+
+
+def test_skinny_integer_bitwise():
+    import tiled_gemm_02_amd as tg
+    p = make_int_problem(640, 128, 512, F16, NN, -2, 2, seed=3)
+    r, got, ref = check_full(p, options=dict(path=tg.TG_PATH_SKINNY))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_skinny_is_chosen_for_the_narrow_workload():
+    import tiled_gemm_02_amd as tg
+    assert tg.tg_gemm_plan(8192, 128, 8192, F16, NN)["path"] == tg.TG_PATH_SKINNY
+
+
+# ---------------------------------------------------------------- GEMV path
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("trans", TRANS)
+@pytest.mark.parametrize("shape", [(1, 1024, 512), (1, 520, 33), (1000, 1, 512), (77, 1, 1031),
+                                   (1, 1, 300)])
+def test_gemv(dtype, trans, shape):
+    import tiled_gemm_02_amd as tg
+    M, N, K = shape
+    _say("case gemv", dtype, trans, shape)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=9)
+    assert tg.tg_gemm_plan(M, N, K, dtype, trans)["path"] == tg.TG_PATH_GEMV
+    r, _, _ = check_full(p)
+    assert r["ok"], r
+    r, _, _ = check_full(p, epilogue="leaky_relu")
+    assert r["ok"], r
+
+
+def test_gemv_strided():
+    p = make_problem(1, 600, 256, F16, NN, "uniform", seed=10, ld_pad=8)
+    r, _, _ = check_full(p, out_pad=0)
+    assert r["ok"], r
+    p = make_problem(300, 1, 256, F16, TT, "uniform", seed=10, ld_pad=4)
+    r, _, _ = check_full(p)
+    assert r["ok"], r
+
+
+# ---------------------------------------------------------------- the measured workloads
+
+@pytest.mark.parametrize("name", ["f32_256", "f16_skinny_8192x128x8192", "f16_gemv_1x8192x8192"])
+def test_workload_full(name):
+    w = dict(WORKLOADS[name])
+    _say("workload full", name)
+    epi = w.pop("epilogue", None)
+    slope = w.pop("slope", 0.01)
+    p = make_problem(**w)
+    r, _, _ = check_full(p, epilogue=epi, slope=slope)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("name", ["f16_4096_nt", "f16_8192", "bf16_leaky_8192",
+                                  "bf16_leaky_6912x2048x4096"])
+def test_workload_sampled(name):
+    w = dict(WORKLOADS[name])
+    _say("workload sampled", name)
+    epi = w.pop("epilogue", None)
+    slope = w.pop("slope", 0.01)
+    p = make_problem(**w)
+    r = check_sampled(p, epilogue=epi, slope=slope)
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("N", [1536, 1544, 3584, 3592, 6144])
+def test_sweep_shapes_sampled(N):
+    _say("sweep", N)
+    p = make_problem(2304, N, 4096, F16, NN, "normal", seed=0)
+    r = check_sampled(p, n=2048)
+    assert r["ok"], r
+    r = check_sampled(p, n=1024, options=dict(tile_m=256, tile_n=128, split_k=1))
+    assert r["ok"], r

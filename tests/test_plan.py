@@ -1,0 +1,112 @@
+"""The planner's tile/wave quantization model (CPU only).
+
+Pins: the integer figures of "Matrix Multiplication Background User's Guide"
+sections 2-3 (A100 with 108 SMs, one 256x128 tile per SM per wave), the
+arithmetic intensities of its section 2, the grid ceil-division of the GEMM
+kernels note, and properties of the MI355X plans.
+"""
+from __future__ import annotations
+
+import pytest
+
+import tiled_gemm_02_amd as tg
+
+F16 = tg.TG_F16
+FORCE_256x128 = dict(tile_m=256, tile_n=128, split_k=1)
+
+
+def a100(M, N, K, tile=(256, 128)):
+    return tg.tg_plan_model(M, N, K, F16, tg.TG_NN, num_cus=108, occupancy=1,
+                            options=dict(tile_m=tile[0], tile_n=tile[1], split_k=1))
+
+
+def test_arithmetic_intensity_examples():
+    # section 2: 8192 x 128 x 8192 -> 124.1 FLOP/B; 8192^3 -> 2730; GEMV < 1
+    assert round(tg.tg_plan_model(8192, 128, 8192, F16)["arith_intensity"], 1) == 124.1
+    assert int(tg.tg_plan_model(8192, 8192, 8192, F16)["arith_intensity"]) == 2730
+    assert tg.tg_plan_model(1, 8192, 8192, F16)["arith_intensity"] < 1
+    assert tg.tg_plan_model(8192, 1, 8192, F16)["arith_intensity"] < 1
+
+
+def test_wave_quantization_fig8():
+    # M = 2304, K = 4096, 256x128 tiles, 108 SMs: N = 1536 is one full wave of 108 tiles
+    p = a100(2304, 1536, 4096)
+    assert p["tiles"] == 108 and p["waves"] == 1 and p["wave_eff"] == 1.0
+    # N = 1544 .. 1664: 9 x 13 = 117 tiles, a tail wave of 9 tiles (8.33% of the SMs)
+    for N in (1544, 1600, 1664):
+        p = a100(2304, N, 4096)
+        assert p["tiles"] == 117 and p["waves"] == 2
+        assert p["tiles"] - 108 == 9 and round(9 / 108 * 100, 2) == 8.33
+    # throughput roughly halves from 1536 to 1544 (time doubles)
+    assert a100(2304, 1544, 4096)["pred_us"] == pytest.approx(2 * a100(2304, 1536, 4096)["pred_us"])
+    # the same step after 3072, 4608 and 6144
+    for n0 in (3072, 4608, 6144):
+        assert a100(2304, n0 + 8, 4096)["waves"] == a100(2304, n0, 4096)["waves"] + 1
+
+
+def test_tile_quantization_fig7():
+    # M = 27648, K = 4096, forced 256x128: N = 136..256 keeps 2 tiles per row, 216 tiles
+    for N in range(136, 257, 8):
+        p = a100(27648, N, 4096)
+        assert p["tiles"] == 216
+    assert a100(27648, 128, 4096)["tiles"] == 108
+    # at N = 136 only 8 of the second tile's 128 columns are useful
+    p = a100(27648, 136, 4096)
+    assert p["tile_eff"] == pytest.approx(136 / 256)
+    assert (136 - 128) / 128 == 0.0625
+    # time is flat while the tile count is flat
+    assert a100(27648, 136, 4096)["pred_us"] == pytest.approx(a100(27648, 256, 4096)["pred_us"])
+
+
+def test_tile_quantization_fig6():
+    # 128x128 tiles: 256x256 -> 4 tiles, 257x256 -> 6 tiles: 1.5x the math for +0.39% work
+    a = a100(256, 256, 1024, tile=(128, 128))
+    b = a100(257, 256, 1024, tile=(128, 128))
+    assert a["tiles"] == 4 and b["tiles"] == 6
+    assert b["tiles"] / a["tiles"] == 1.5
+    assert round((257 * 256 / (256 * 256) - 1) * 100, 2) == 0.39
+
+
+def test_tile_sizes_fig5():
+    # 6912 x 2048: 256x128 gives 432 = 4 x 108 tiles; 64x64 gives 8x the tiles
+    big = a100(6912, 2048, 4096, tile=(256, 128))
+    small = a100(6912, 2048, 4096, tile=(64, 64))
+    assert big["tiles"] == 432 == 4 * 108
+    assert small["tiles"] == 8 * big["tiles"]
+
+
+def test_grid_is_ceil_division():
+    # 16 x 16 blocks over N = 1000: (1000 + 15) / 16 = 63 blocks per dimension
+    p = tg.tg_plan_model(1000, 1000, 64, F16, tg.TG_NN, num_cus=108, occupancy=1,
+                         options=dict(tile_m=16, tile_n=16, split_k=1))
+    assert p["tiles"] == 63 * 63 == ((1000 + 15) // 16) ** 2
+
+
+def test_mi355x_plans():
+    p = tg.tg_plan_model(8192, 8192, 8192, F16)
+    assert p["path_name"] == "mfma" and p["tile_m"] * p["tile_n"] == 256 * 256
+    assert p["tiles"] == 1024 and p["waves"] == 4 and p["wave_eff"] == 1.0
+    p = tg.tg_plan_model(1, 8192, 8192, F16)
+    assert p["path_name"] == "gemv"
+    p = tg.tg_plan_model(8192, 1, 8192, F16)
+    assert p["path_name"] == "gemv"
+    # K == 0 and empty outputs are quick returns
+    assert tg.tg_plan_model(64, 64, 0, F16)["path_name"] == "none"
+    assert tg.tg_plan_model(0, 64, 64, F16)["path_name"] == "none"
+    # small M and N with large K split K
+    p = tg.tg_plan_model(256, 256, 65536, F16)
+    assert p["split_k"] > 1 and p["workspace_bytes"] == p["split_k"] * 256 * 256 * 4
+    # on 256 CUs a forced 256x128 tile steps from one to two waves between N = 3584 and 3592
+    f = dict(tile_m=256, tile_n=128, split_k=1)
+    a = tg.tg_plan_model(2304, 3584, 4096, F16, occupancy=1, options=f)
+    b = tg.tg_plan_model(2304, 3592, 4096, F16, occupancy=1, options=f)
+    assert (a["tiles"], a["waves"], b["tiles"], b["waves"]) == (252, 1, 261, 2)
+
+
+def test_flop_formula_against_page_numbers():
+    # Triton tutorial, T4: 2*M*N*K FLOP over the median latency.  Its X is 8192 x 6144 and Y is
+    # 6144 x 4096 (BLAS M = 8192, K = 6144, N = 4096); 130.7831 ms -> 3.1533 TFLOPS and
+    # 261.9420 ms -> 1.5741 TFLOPS (printed means of per-run ratios; agree to 3 digits).
+    flop = 2 * 8192 * 4096 * 6144
+    assert flop / 130.7831e-3 / 1e12 == pytest.approx(3.1533, rel=2e-3)
+    assert flop / 261.9420e-3 / 1e12 == pytest.approx(1.5741, rel=1e-3)

@@ -58,6 +58,15 @@ hipError_t launch_fill_zero(int dtype, void *C, int M, int N, int64_t ldc, hipSt
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F16: return launch_skinny_f16(trans_b, a, s);
+    case TG_BF16: return launch_skinny_bf16(trans_b, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemv(int dtype, bool rows_form, bool vec, const GemvArgs &a, hipStream_t s)
 {
     switch (dtype) {
@@ -257,6 +266,31 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         const int cb = elem_bytes(p.dtype);
         a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
         e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);
+        if (e == hipSuccess && pl.split_k > 1)
+            e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, (int)p.M, (int)p.N, C,
+                                     p.ldc, epi_kind, slope, a.c_vec, s);
+    } else if (pl.path == TG_PATH_SKINNY) {
+        SkinnyArgs a{};
+        a.A = A;
+        a.B = B;
+        a.C = C;
+        a.ws = (float *)ws;
+        a.lda = p.lda;
+        a.ldb = p.ldb;
+        a.ldc = p.ldc;
+        a.M = (int)p.M;
+        a.N = (int)p.N;
+        a.K = (int)p.K;
+        const int BK = pl.tile_k;
+        int64_t kps = (p.K + pl.split_k - 1) / pl.split_k;
+        kps = (kps + BK - 1) / BK * BK;
+        a.kps = (int)kps;
+        a.splits = pl.split_k;
+        a.epi = epi_kind;
+        a.slope = slope;
+        const int cb = elem_bytes(p.dtype);
+        a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
+        e = launch_skinny(p.dtype, (p.trans & TG_TRANS_B) != 0, a, s);
         if (e == hipSuccess && pl.split_k > 1)
             e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, (int)p.M, (int)p.N, C,
                                      p.ldc, epi_kind, slope, a.c_vec, s);

@@ -27,6 +27,11 @@ __device__ __forceinline__ float apply_epi(float x, int epi, float slope)
     return (epi == kEpiLeaky && x < 0.0f) ? x * slope : x;
 }
 
+// Bit reinterpretation of one 32-bit lane value.  The argument is taken by
+// value: bit-casting a vector-element expression (v[i]) directly has been seen
+// to read element 0 whatever i is, so callers copy the element out first.
+__device__ __forceinline__ float u32_as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 // ---------------------------------------------------------------- storage types
 //
 // Each trait describes one storage type: its element, how many elements a
@@ -88,8 +93,10 @@ __device__ __forceinline__ void mfma_chunk<F32>(f32x4 &acc, const u32x4 &bop, co
 {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, bop[e]),
-                                                   __builtin_bit_cast(float, aop[e]), acc, 0, 0, 0);
+    {
+        const uint32_t b = bop[e], a = aop[e];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(u32_as_f32(b), u32_as_f32(a), acc, 0, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------- small helpers

@@ -45,8 +45,10 @@ __device__ __forceinline__ void unpack(const u32x4 &c, float *f)
 {
     if constexpr (Tr::kBytes == 4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            f[e] = __builtin_bit_cast(float, c[e]);
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = c[e];
+            f[e] = u32_as_f32(w);
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {

@@ -7,6 +7,7 @@
 
 #include "gemv.hpp"
 #include "mfma_gemm.hpp"
+#include "skinny.hpp"
 
 namespace tg {
 
@@ -20,6 +21,7 @@ hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, i
 hipError_t launch_fill_zero(int dtype, void *C, int M, int N, int64_t ldc, hipStream_t s);
 // rows_form: outputs are contiguous dot products; else column streaming.
 hipError_t launch_gemv(int dtype, bool rows_form, bool vec, const GemvArgs &a, hipStream_t s);
+hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream_t s);
 
 #define TG_DECLARE_TYPE_LAUNCHERS(NAME)                                                          \
     hipError_t launch_mfma_##NAME(int trans, int bm, int bn, bool vec, const MfmaArgs &a,        \
@@ -29,7 +31,8 @@ hipError_t launch_gemv(int dtype, bool rows_form, bool vec, const GemvArgs &a, h
                                            int64_t ldc, int epi, float slope, int c_vec,         \
                                            hipStream_t s);                                       \
     hipError_t launch_fill_zero_##NAME(void *C, int M, int N, int64_t ldc, hipStream_t s);       \
-    hipError_t launch_gemv_##NAME(bool rows_form, bool vec, const GemvArgs &a, hipStream_t s);
+    hipError_t launch_gemv_##NAME(bool rows_form, bool vec, const GemvArgs &a, hipStream_t s);    \
+    hipError_t launch_skinny_##NAME(bool trans_b, const SkinnyArgs &a, hipStream_t s);
 
 TG_DECLARE_TYPE_LAUNCHERS(f16)
 TG_DECLARE_TYPE_LAUNCHERS(bf16)

@@ -307,8 +307,8 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
 
 static bool skinny_fits(const Problem &p)
 {
-    return p.dtype != TG_F32 && p.N <= kSkinnyMaxN && p.N >= 2 && p.M >= 2 * kSkinnyRows &&
-           vec_ok(p) && !(p.trans & TG_TRANS_A) && !(p.trans & TG_TRANS_B);
+    return p.dtype != TG_F32 && p.N <= kSkinnyMaxN && p.N >= 8 && p.M >= 2 * kSkinnyRows &&
+           vec_ok(p) && !(p.trans & TG_TRANS_A);
 }
 
 static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opts, tg_plan *out,
@@ -319,17 +319,18 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
         return TG_ERR_UNSUPPORTED;
     }
     if (!skinny_fits(p)) {
-        *why = "skinny path needs 16-bit NN operands, 2 <= N <= 128, M >= 128, 16-byte aligned";
+        *why = "skinny path needs 16-bit operands, A not transposed, 8 <= N <= 128, M >= 128, "
+               "dimensions and leading dimensions multiples of 8, 16-byte aligned";
         return TG_ERR_UNSUPPORTED;
     }
-    const int BK = 64;
+    const int BK = kSkinnyBK;
     const int64_t tm = (p.M + kSkinnyRows - 1) / kSkinnyRows;
     // split K until the grid covers every CU about twice, one BK step per split at least
     int s = 1;
     if (opts && opts->split_k > 0) {
         s = opts->split_k;
     } else {
-        while (tm * s < 2LL * chip.num_cus && (int64_t)(s * 2) * 4 * BK <= p.K && s < 16)
+        while (tm * s < (int64_t)chip.num_cus && (int64_t)(s * 2) * 2 * BK <= p.K && s < 16)
             s *= 2;
     }
     int64_t kps = (p.K + s - 1) / s;
@@ -340,7 +341,7 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
     out->tile_n = kSkinnyMaxN;
     out->tile_k = BK;
     out->split_k = s;
-    out->occupancy = 2;
+    out->occupancy = 1;
     out->vector_io = 1;
     out->tiles = tm;
     out->workgroups = tm * s;
@@ -387,6 +388,8 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
         return TG_OK;
     }
     int path = opts ? opts->path : TG_PATH_AUTO;
+    if (path == TG_PATH_AUTO && opts && (opts->tile_m > 0 || opts->tile_n > 0))
+        path = TG_PATH_MFMA;  // a forced macro tile means the macro-tile kernel
     if (path == TG_PATH_AUTO) {
         const double ridge = chip_peak(chip, p.dtype) / (chip.hbm_gbs * 1e9);
         if (p.M == 1 || p.N == 1)

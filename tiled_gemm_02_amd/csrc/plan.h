@@ -49,7 +49,8 @@ int model_occupancy(int dtype, int bm, int bn, bool vec);
 // Skinny kernel geometry (N <= kSkinnyMaxN).
 constexpr int kSkinnyRows = 64;    // output rows per workgroup
 constexpr int kSkinnyMaxN = 128;   // widest output it covers in one pass
-constexpr bool kSkinnyEnabled = false;
+constexpr int kSkinnyBK = 256;     // K per step
+constexpr bool kSkinnyEnabled = true;
 
 // Occupancy lookup: returns workgroups per CU for a tile kernel; the device
 // path fills this from the runtime, the model from model_occupancy().
