@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -25,6 +26,51 @@ hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, const Mfm
     case TG_F32: return launch_mfma_f32(trans, bm, bn, vec, a, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F16: return launch_mfma2_f16(trans, bm, bn, a, s);
+    case TG_BF16: return launch_mfma2_bf16(trans, bm, bn, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+int mfma2_occupancy(int dtype, int trans, int bm, int bn)
+{
+    switch (dtype) {
+    case TG_F16: return mfma2_occupancy_f16(trans, bm, bn);
+    case TG_BF16: return mfma2_occupancy_bf16(trans, bm, bn);
+    }
+    return 0;
+}
+
+// Kernel generation for 16-bit aligned operands: 2 = LDS-DMA pipeline
+// (default), 1 = register-staged kernel.  TG_MFMA_VARIANT overrides it, for
+// side-by-side timing.
+static int mfma_variant()
+{
+    static int v = [] {
+        const char *e = getenv("TG_MFMA_VARIANT");
+        return (e && e[0] == '1') ? 1 : 2;
+    }();
+    return v;
+}
+
+// The LDS-DMA kernel addresses operands with 32-bit element offsets.
+static bool fits_u32(int64_t rows, int64_t ld, int64_t cols)
+{
+    return rows <= 0 || (rows - 1) * ld + cols < ((int64_t)1 << 32);
+}
+
+static bool use_mfma2(int dtype, int trans, bool vec, int64_t M, int64_t N, int64_t K, int64_t lda,
+                      int64_t ldb)
+{
+    if (dtype == TG_F32 || !vec || mfma_variant() != 2)
+        return false;
+    const bool ta = trans & TG_TRANS_A, tb = trans & TG_TRANS_B;
+    return fits_u32(ta ? K : M, lda, ta ? M : K) && fits_u32(tb ? N : K, ldb, tb ? K : N);
 }
 
 int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec)
@@ -161,7 +207,8 @@ static int device_occ(int dtype, int trans, int bm, int bn, bool vec, void *ctx)
     std::lock_guard<std::mutex> lk(g_dev_mu);
     int &slot = d->occ[dtype][trans][ts][vec ? 1 : 0];
     if (slot == 0) {
-        int n = mfma_occupancy(dtype, trans, bm, bn, vec);
+        int n = (dtype != TG_F32 && vec && mfma_variant() == 2) ? mfma2_occupancy(dtype, trans, bm, bn)
+                                                                  : mfma_occupancy(dtype, trans, bm, bn, vec);
         slot = n > 0 ? n : -1;
     }
     return slot > 0 ? slot : model_occupancy(dtype, bm, bn, vec);
@@ -265,7 +312,10 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.slope = slope;
         const int cb = elem_bytes(p.dtype);
         a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
-        e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);
+        if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, p.M, p.N, p.K, p.lda, p.ldb))
+            e = launch_mfma2(p.dtype, p.trans, pl.tile_m, pl.tile_n, a, s);
+        else
+            e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);
         if (e == hipSuccess && pl.split_k > 1)
             e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, (int)p.M, (int)p.N, C,
                                      p.ldc, epi_kind, slope, a.c_vec, s);

@@ -3,5 +3,6 @@
 #define TG_TRAIT BF16
 #define TG_NAME bf16
 #define TG_TILE_LIST TG_TILE(256, 256) TG_TILE(256, 128) TG_TILE(128, 128) TG_TILE(128, 64) TG_TILE(64, 64)
+#define TG_HAS_MFMA2 1
 #define TG_HAS_SKINNY 1
 #include "instances.inc"

@@ -16,6 +16,9 @@ hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, const Mfm
                        hipStream_t s);
 // Resident workgroups per CU of an instance (0 if none).
 int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec);
+// The LDS-DMA kernel for 16-bit, 16-byte-aligned operands (same tiles).
+hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s);
+int mfma2_occupancy(int dtype, int trans, int bm, int bn);
 hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, int N, void *C,
                                 int64_t ldc, int epi, float slope, int c_vec, hipStream_t s);
 hipError_t launch_fill_zero(int dtype, void *C, int M, int N, int64_t ldc, hipStream_t s);
@@ -32,7 +35,9 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
                                            hipStream_t s);                                       \
     hipError_t launch_fill_zero_##NAME(void *C, int M, int N, int64_t ldc, hipStream_t s);       \
     hipError_t launch_gemv_##NAME(bool rows_form, bool vec, const GemvArgs &a, hipStream_t s);    \
-    hipError_t launch_skinny_##NAME(bool trans_b, const SkinnyArgs &a, hipStream_t s);
+    hipError_t launch_skinny_##NAME(bool trans_b, const SkinnyArgs &a, hipStream_t s);           \
+    hipError_t launch_mfma2_##NAME(int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s); \
+    int mfma2_occupancy_##NAME(int trans, int bm, int bn);
 
 TG_DECLARE_TYPE_LAUNCHERS(f16)
 TG_DECLARE_TYPE_LAUNCHERS(bf16)
