@@ -36,7 +36,7 @@ ROTATE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["tiled_gemm_02_amd/csrc/kernels/common.hpp",
                   "tiled_gemm_02_amd/csrc/kernels/mfma_gemm.hpp",
-                  "tiled_gemm_02_amd/csrc/kernels/mfma_gemm2.hpp",
+                  "tiled_gemm_02_amd/csrc/kernels/mfma_gemm3.hpp",
                   "tiled_gemm_02_amd/csrc/kernels/gemv.hpp",
                   "tiled_gemm_02_amd/csrc/kernels/skinny.hpp",
                   "tiled_gemm_02_amd/csrc/kernels/aux_kernels.hpp"]

@@ -234,6 +234,27 @@ def test_gemv(dtype, trans, shape):
     assert r["ok"], r
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("lanes", [8, 16, 32, 64])
+@pytest.mark.parametrize("split", [1, 3, 16])
+def test_gemv_strip_widths_and_splits(dtype, lanes, split):
+    """Every strip width of the vector cols kernel, with and without K splits
+    (the partial-sum reduction), on a ragged K and a column count that leaves a
+    partial last strip."""
+    import tiled_gemm_02_amd as tg
+    E = 4 if dtype == F32 else 8
+    N = lanes * E * 5 + 2 * E
+    _say("case gemv strips", dtype, lanes, split, N)
+    p = make_problem(1, N, 1037, dtype, NN, "uniform", seed=12)
+    opts = dict(path=tg.TG_PATH_GEMV, tile_n=lanes * E, split_k=split)
+    pl = tg.tg_gemm_plan(1, N, 1037, dtype, NN, opts)
+    assert pl["tile_n"] == lanes * E and pl["split_k"] == split and pl["vector_io"] == 1, pl
+    r, _, _ = check_full(p, options=opts)
+    assert r["ok"], r
+    r, _, _ = check_full(p, epilogue="leaky_relu", options=opts)
+    assert r["ok"], r
+
+
 def test_gemv_strided():
     p = make_problem(1, 600, 256, F16, NN, "uniform", seed=10, ld_pad=8)
     r, _, _ = check_full(p, out_pad=0)

@@ -58,19 +58,16 @@ static int mfma_variant()
     return v;
 }
 
-// The LDS-DMA kernel addresses operands with 32-bit element offsets.
-static bool fits_u32(int64_t rows, int64_t ld, int64_t cols)
-{
-    return rows <= 0 || (rows - 1) * ld + cols < ((int64_t)1 << 32);
-}
-
+// The LDS-DMA kernel addresses each lane's copy with a 32-bit byte offset from
+// a per-tile 64-bit base: at most 256 rows (or 64 K-rows) of one operand, so a
+// leading dimension up to 2^22 elements keeps every offset below 2^31.
 static bool use_mfma2(int dtype, int trans, bool vec, int64_t M, int64_t N, int64_t K, int64_t lda,
                       int64_t ldb)
 {
+    (void)trans; (void)M; (void)N; (void)K;
     if (dtype == TG_F32 || !vec || mfma_variant() != 2)
         return false;
-    const bool ta = trans & TG_TRANS_A, tb = trans & TG_TRANS_B;
-    return fits_u32(ta ? K : M, lda, ta ? M : K) && fits_u32(tb ? N : K, ldb, tb ? K : N);
+    return lda <= (int64_t(1) << 22) && ldb <= (int64_t(1) << 22);
 }
 
 int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec)
@@ -113,12 +110,12 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(int dtype, bool rows_form, bool vec, const GemvArgs &a, hipStream_t s)
+hipError_t launch_gemv(int dtype, bool rows_form, bool vec, int lpr, const GemvArgs &a, hipStream_t s)
 {
     switch (dtype) {
-    case TG_F16: return launch_gemv_f16(rows_form, vec, a, s);
-    case TG_BF16: return launch_gemv_bf16(rows_form, vec, a, s);
-    case TG_F32: return launch_gemv_f32(rows_form, vec, a, s);
+    case TG_F16: return launch_gemv_f16(rows_form, vec, lpr, a, s);
+    case TG_BF16: return launch_gemv_bf16(rows_form, vec, lpr, a, s);
+    case TG_F32: return launch_gemv_f32(rows_form, vec, lpr, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -379,8 +376,8 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         } else {
             g.rows_per_split = (int)p.K;
         }
-        (void)E;
-        e = launch_gemv(p.dtype, rows_form, pl.vector_io != 0, g, s);
+        const int lpr = rows_form ? 0 : pl.tile_n / E;
+        e = launch_gemv(p.dtype, rows_form, pl.vector_io != 0, lpr, g, s);
     } else {
         return fail(TG_ERR_UNSUPPORTED, "path %d has no kernel", pl.path);
     }

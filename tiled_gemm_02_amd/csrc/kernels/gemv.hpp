@@ -58,11 +58,105 @@ __device__ __forceinline__ void unpack(const u32x4 &c, float *f)
     }
 }
 
-// cols form.  Grid: x = column strips of 64 chunks (64*E columns), y = K-splits.
-// The 4 waves of a workgroup take interleaved rows of the split's K range and
-// are summed in wave order through LDS.
-template <typename Tr, bool VEC>
+// cols form, vector path.  A workgroup owns one strip of LPR * E columns
+// (each lane 16 bytes of a row, LPR lanes per row, so a row segment is LPR x
+// 16 bytes) over a K range; its 256 lanes cover 256 / LPR rows per load, and
+// each lane keeps 8 rows in flight.  The matrix is read once, so its loads are
+// non-temporal (they do not displace cached data).  Partial column sums are
+// combined across the lanes of a wave by a butterfly over the row-selecting
+// lane bits, then across the 4 waves in wave order; with one K range the
+// result is final, otherwise it is a partial for the reduction kernel.
+template <typename Tr, int LPR>
 __global__ __launch_bounds__(256) void gemv_cols_kernel(GemvArgs p)
+{
+    using T = typename Tr::T;
+    constexpr int E = Tr::E;
+    constexpr int RPW = 64 / LPR;    // row slots per wave
+    constexpr int SLOTS = 4 * RPW;   // row slots per workgroup
+    constexpr int U = 8;             // rows in flight per lane
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int q = lane % LPR;
+    const int slot = wave * RPW + lane / LPR;
+    const int col = (blockIdx.x * LPR + q) * E;
+    const int k_lo = blockIdx.y * p.rows_per_split;
+    const int k_hi = min(p.K, k_lo + p.rows_per_split);
+    const T *base = (const T *)p.X + col;
+
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        acc[e] = 0.f;
+
+    // n is a multiple of E on this path, so a chunk is wholly in or out
+    if (col < p.n) {
+        int k = k_lo + slot;
+        for (; k + (U - 1) * SLOTS < k_hi; k += U * SLOTS) {
+            u32x4 x[U];
+            float a[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                x[u] = __builtin_nontemporal_load((const u32x4 *)(base + (int64_t)(k + u * SLOTS) * p.ldx));
+                a[u] = load_scalar<Tr>(p.V, (int64_t)(k + u * SLOTS) * p.vs);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float f[E];
+                unpack<Tr>(x[u], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    acc[e] += a[u] * f[e];
+            }
+        }
+        for (; k < k_hi; k += SLOTS) {
+            const u32x4 x = __builtin_nontemporal_load((const u32x4 *)(base + (int64_t)k * p.ldx));
+            const float a = load_scalar<Tr>(p.V, (int64_t)k * p.vs);
+            float f[E];
+            unpack<Tr>(x, f);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                acc[e] += a * f[e];
+        }
+    }
+
+    // lanes q, q + LPR, q + 2 LPR, ... hold the same columns
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            acc[e] += __shfl_xor(acc[e], off, 64);
+
+    __shared__ float red[4][LPR * E];
+    if (lane < LPR) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            red[wave][lane * E + e] = acc[e];
+    }
+    __syncthreads();
+    if (wave != 0 || lane >= LPR || col >= p.n)
+        return;
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        s[e] = ((red[0][lane * E + e] + red[1][lane * E + e]) + red[2][lane * E + e]) +
+               red[3][lane * E + e];
+    if (p.ksplit > 1) {
+        float *W = p.ws + (int64_t)blockIdx.y * p.n + col;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            W[e] = s[e];
+    } else {
+        T *O = (T *)p.O;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            O[(int64_t)(col + e) * p.os] = Tr::from_f32(apply_epi(s[e], p.epi, p.slope));
+    }
+}
+
+// cols form, element-wise path (unaligned or ragged operands).  Grid: x =
+// strips of 64 * E columns, y = K-splits; the 4 waves take interleaved rows of
+// the split's K range and are summed in wave order through LDS.
+template <typename Tr>
+__global__ __launch_bounds__(256) void gemv_cols_generic_kernel(GemvArgs p)
 {
     using T = typename Tr::T;
     constexpr int E = Tr::E;
@@ -76,39 +170,8 @@ __global__ __launch_bounds__(256) void gemv_cols_kernel(GemvArgs p)
 #pragma unroll
     for (int e = 0; e < E; ++e)
         acc[e] = 0.f;
-
     const bool col_in = col < p.n;
-    if (VEC && col_in) {
-        const T *base = X + col;
-        int k = k_lo + wave;
-        // 8 rows in flight per lane
-        for (; k + 28 < k_hi; k += 32) {
-            u32x4 x[8];
-            float a[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                x[u] = *(const u32x4 *)(base + (int64_t)(k + 4 * u) * p.ldx);
-                a[u] = load_scalar<Tr>(p.V, (int64_t)(k + 4 * u) * p.vs);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                float f[E];
-                unpack<Tr>(x[u], f);
-#pragma unroll
-                for (int e = 0; e < E; ++e)
-                    acc[e] += a[u] * f[e];
-            }
-        }
-        for (; k < k_hi; k += 4) {
-            const u32x4 x = *(const u32x4 *)(base + (int64_t)k * p.ldx);
-            const float a = load_scalar<Tr>(p.V, (int64_t)k * p.vs);
-            float f[E];
-            unpack<Tr>(x, f);
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                acc[e] += a * f[e];
-        }
-    } else if (col_in) {
+    if (col_in) {
         for (int k = k_lo + wave; k < k_hi; k += 4) {
             const float a = load_scalar<Tr>(p.V, (int64_t)k * p.vs);
 #pragma unroll
@@ -154,9 +217,21 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(GemvArgs p)
     const int j = blockIdx.x * 256 + threadIdx.x;
     if (j >= p.n)
         return;
+    const float *w = p.ws + j;
     float s = 0.f;
-    for (int z = 0; z < p.ksplit; ++z)
-        s += p.ws[(int64_t)z * p.n + j];
+    int z = 0;
+    // eight independent loads in flight, summed in increasing z
+    for (; z + 8 <= p.ksplit; z += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = w[(int64_t)(z + u) * p.n];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            s += v[u];
+    }
+    for (; z < p.ksplit; ++z)
+        s += w[(int64_t)z * p.n];
     ((T *)p.O)[(int64_t)j * p.os] = Tr::from_f32(apply_epi(s, p.epi, p.slope));
 }
 
@@ -180,7 +255,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs p)
         u32x4 x[4], v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            x[u] = *(const u32x4 *)(row + (int64_t)(c + 64 * u) * E);
+            x[u] = __builtin_nontemporal_load((const u32x4 *)(row + (int64_t)(c + 64 * u) * E));
             v[u] = *(const u32x4 *)(V + (int64_t)(c + 64 * u) * E);
         }
 #pragma unroll

@@ -23,7 +23,10 @@ hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, i
                                 int64_t ldc, int epi, float slope, int c_vec, hipStream_t s);
 hipError_t launch_fill_zero(int dtype, void *C, int M, int N, int64_t ldc, hipStream_t s);
 // rows_form: outputs are contiguous dot products; else column streaming.
-hipError_t launch_gemv(int dtype, bool rows_form, bool vec, const GemvArgs &a, hipStream_t s);
+// lpr: lanes per row segment of the vector cols kernel (columns per workgroup = lpr x
+// elements per 16 bytes).
+hipError_t launch_gemv(int dtype, bool rows_form, bool vec, int lpr, const GemvArgs &a,
+                       hipStream_t s);
 hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream_t s);
 
 #define TG_DECLARE_TYPE_LAUNCHERS(NAME)                                                          \
@@ -34,7 +37,8 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
                                            int64_t ldc, int epi, float slope, int c_vec,         \
                                            hipStream_t s);                                       \
     hipError_t launch_fill_zero_##NAME(void *C, int M, int N, int64_t ldc, hipStream_t s);       \
-    hipError_t launch_gemv_##NAME(bool rows_form, bool vec, const GemvArgs &a, hipStream_t s);    \
+    hipError_t launch_gemv_##NAME(bool rows_form, bool vec, int lpr, const GemvArgs &a,          \
+                                  hipStream_t s);                                                \
     hipError_t launch_skinny_##NAME(bool trans_b, const SkinnyArgs &a, hipStream_t s);           \
     hipError_t launch_mfma2_##NAME(int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s); \
     int mfma2_occupancy_##NAME(int trans, int bm, int bn);

@@ -145,14 +145,46 @@ static int plan_gemv(const Problem &p, const Chip &chip, const tg_options *opts,
         const int64_t ldx = (p.M == 1) ? p.ldb : p.lda;
         out->vector_io = p.ptrs_aligned && vs == 1 && ldx % E == 0 && p.K % E == 0;
     } else {
-        const int64_t cols_per_wg = 64LL * E;
+        const int64_t ldx = (p.M == 1) ? p.ldb : p.lda;
+        const bool vec = p.ptrs_aligned && n % E == 0 && ldx % E == 0;
+        int64_t cols_per_wg = 64LL * E;  // element-wise kernel: 64 lanes x E columns
+        int64_t rows_per_pass = 4;       // rows its workgroup covers per load
+        if (vec) {
+            // vector kernel: strips of lpr lanes x 16 bytes.  Wide row segments
+            // (a wave reads up to 1 KiB of a row) keep the stream close to
+            // sequential; the K split then gives every CU a workgroup, and the
+            // narrower strips serve outputs too short for a full one.
+            int lpr = 0;
+            if (opts && opts->tile_n > 0) {
+                lpr = opts->tile_n / E;
+                if (lpr * E != opts->tile_n || (lpr != 8 && lpr != 16 && lpr != 32 && lpr != 64)) {
+                    *why = "GEMV strips are 8, 16, 32 or 64 lanes of 16 bytes wide";
+                    return TG_ERR_UNSUPPORTED;
+                }
+            } else {
+                // 512-byte row segments measured fastest at 1 x 8192 x 8192
+                lpr = 32;
+                while (lpr > 8 && (int64_t)lpr * E / 2 >= n)
+                    lpr /= 2;
+            }
+            cols_per_wg = (int64_t)lpr * E;
+            rows_per_pass = 256 / lpr;
+        }
         const int64_t strips = (n + cols_per_wg - 1) / cols_per_wg;
-        // enough workgroups to keep every CU streaming: about 8 per CU
-        const int64_t want = 8LL * chip.num_cus;
-        int64_t ks = std::max<int64_t>(1, (want + strips - 1) / strips);
-        ks = std::min<int64_t>(ks, std::max<int64_t>(1, p.K / 32));
-        if (opts && opts->split_k > 0)
+        int64_t ks;
+        if (opts && opts->split_k > 0) {
             ks = std::min<int64_t>(opts->split_k, std::max<int64_t>(1, p.K));
+        } else if (vec) {
+            // about two workgroups per CU, each lane keeping 8 rows in flight;
+            // keep at least that many rows per split
+            ks = std::max<int64_t>(1, (2LL * chip.num_cus + strips - 1) / strips);
+            ks = std::min<int64_t>(ks, std::max<int64_t>(1, p.K / (8 * rows_per_pass)));
+        } else {
+            // element-wise kernel: about 8 workgroups per CU
+            const int64_t want = 8LL * chip.num_cus;
+            ks = std::max<int64_t>(1, (want + strips - 1) / strips);
+            ks = std::min<int64_t>(ks, std::max<int64_t>(1, p.K / 32));
+        }
         int64_t rps = (p.K + ks - 1) / ks;
         rps = (rps + 3) / 4 * 4;
         ks = (p.K + rps - 1) / rps;
@@ -162,8 +194,7 @@ static int plan_gemv(const Problem &p, const Chip &chip, const tg_options *opts,
         out->tiles = strips;
         out->workgroups = strips * ks;
         out->workspace_bytes = ks > 1 ? (uint64_t)ks * (uint64_t)n * 4u : 0;
-        const int64_t ldx = (p.M == 1) ? p.ldb : p.lda;
-        out->vector_io = p.ptrs_aligned && n % E == 0 && ldx % E == 0;
+        out->vector_io = vec ? 1 : 0;
     }
     const int64_t slots = (int64_t)chip.num_cus * out->occupancy;
     out->waves = (out->workgroups + slots - 1) / slots;
