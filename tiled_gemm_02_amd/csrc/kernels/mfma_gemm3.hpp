@@ -52,14 +52,36 @@ namespace tg {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBK3 = 64;   // K per stage (16-bit elements)
+constexpr int kBK3 = 64;   // K per stage (16-bit elements) of the pipelined kernel
 
-__device__ __forceinline__ int kc3_swz(int r) { return r & 6; }
+// Chunk swizzle of a K-contiguous LDS row of KCH 16-byte chunks (KCH = 8:
+// 128-byte rows, 64-deep stages; KCH = 4: 64-byte rows, 32-deep stages).  SW
+// selects the fragment shape the layout serves: 0 for 16 x 16 x 32 MFMA
+// fragments (16 rows x 4 chunks per read), 1 for 32 x 32 x 16 ones (32 rows x
+// 2 chunks per read); each is conflict free for its own reads.
+template <int KCH, int SW = 0>
+__device__ __forceinline__ int kc3_swz(int r)
+{
+    static_assert(KCH == 4 || KCH == 8, "row of 4 or 8 chunks");
+    static_assert(SW == 0 || KCH == 4, "32 x 32 layout only for 64-byte rows");
+    if constexpr (KCH == 8)
+        return r & 6;
+    else if constexpr (SW == 0)
+        return (r >> 1) & 3;
+    else
+        return (r >> 2) & 3;
+}
 
-template <int CH>
+// Chunk swizzle of an M/N-contiguous k-row of CH chunks.  SW = 0: a
+// transposed 16 x 16 x 32 fragment read touches 8 k-rows x 32 bytes per pass,
+// spread by 32-byte steps; SW = 1: a 32 x 32 x 16 one touches 4 k-rows x 64
+// bytes, spread by 64-byte steps.
+template <int CH, int SW = 0>
 __device__ __forceinline__ int mn3_swz(int k)
 {
-    if constexpr (CH >= 16)
+    if constexpr (SW == 1)
+        return (4 * (k & 3)) & (CH - 1);
+    else if constexpr (CH >= 16)
         return (2 * (k & 3) + 8 * ((k >> 3) & 3)) & (CH - 1);
     else
         return (2 * ((k & 3) ^ ((k >> 3) & 3))) & (CH - 1);
@@ -71,6 +93,14 @@ __device__ __forceinline__ void wait_vm_lgkm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// s_waitcnt vmcnt(N) alone (LDS reads may stay in flight).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -116,42 +146,44 @@ __device__ __forceinline__ void mfma_drain()
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 }
 
-// One operand's stage traffic: ROWS tile rows (m for A, n for B).
-// MN: the operand is contiguous along the tile rows in memory.
-template <int ROWS, bool MN>
+// One operand's stage traffic: ROWS tile rows (m for A, n for B) by BKS of K,
+// copied by NW waves.  MN: the operand is contiguous along the tile rows in
+// memory.
+template <int ROWS, bool MN, int NW, int BKS = kBK3, int SW = 0>
 struct Dma3 {
-    static constexpr int PER_WAVE = ROWS / 32;   // 1 KiB copies per wave per stage
-    static constexpr int CH = ROWS / 8;          // chunks per k-row (MN layout)
-    static constexpr int BYTES = ROWS * 128;     // LDS bytes per stage
-    static_assert(ROWS % 32 == 0, "tile rows must be a multiple of 32");
+    static constexpr int BYTES = ROWS * BKS * 2;                // LDS bytes per stage
+    static constexpr int PER_WAVE = BYTES / 1024 / NW;          // 1 KiB copies per wave per stage
+    static constexpr int CH = ROWS / 8;                         // chunks per k-row (MN layout)
+    static constexpr int KCH = BKS / 8;                         // chunks per row (KC layout)
+    static_assert(PER_WAVE >= 1 && PER_WAVE * NW * 1024 == BYTES, "stage does not split over the waves");
 
     const char *base;        // byte address of (row0, kbeg) / (kbeg, row0)
     int64_t step;            // bytes to advance per stage
     uint32_t off[PER_WAVE];  // this lane's byte offsets from base
 
-    __device__ static __forceinline__ int pos(int wave, int lane, int u) { return (wave + 4 * u) * 64 + lane; }
+    __device__ static __forceinline__ int pos(int wave, int lane, int u) { return (wave + NW * u) * 64 + lane; }
 
     __device__ __forceinline__ void init(const uint16_t *X, int64_t ld, int rows_total, int row0,
                                          int kbeg, int wave, int lane)
     {
         if constexpr (!MN) {
             base = (const char *)(X + (int64_t)row0 * ld + kbeg);
-            step = kBK3 * 2;
+            step = BKS * 2;
         } else {
             base = (const char *)(X + (int64_t)kbeg * ld + row0);
-            step = (int64_t)kBK3 * ld * 2;
+            step = (int64_t)BKS * ld * 2;
         }
 #pragma unroll
         for (int u = 0; u < PER_WAVE; ++u) {
             const int P = pos(wave, lane, u);
             if constexpr (!MN) {
-                const int r = P >> 3;
-                const int c = (P & 7) ^ kc3_swz(r);
+                const int r = P / KCH;
+                const int c = (P % KCH) ^ kc3_swz<KCH, SW>(r);
                 const int gr = min(row0 + r, rows_total - 1) - row0;
                 off[u] = (uint32_t)(((int64_t)gr * ld + 8 * c) * 2);
             } else {
                 const int k = P / CH;
-                const int c = (P % CH) ^ mn3_swz<CH>(k);
+                const int c = (P % CH) ^ mn3_swz<CH, SW>(k);
                 const int gc = min(row0 + 8 * c, rows_total - 8) - row0;
                 off[u] = (uint32_t)(((int64_t)k * ld + gc) * 2);
             }
@@ -161,14 +193,18 @@ struct Dma3 {
     // Copy stage t into the LDS region at byte address `dst` (uniform).
     __device__ __forceinline__ void dma(int t, uint32_t dst, int wave) const
     {
-        const char *b = base + (int64_t)t * step;
 #pragma unroll
         for (int u = 0; u < PER_WAVE; ++u)
-            dma16(off[u], b, dst + (uint32_t)(wave + 4 * u) * 1024u);
+            dma_one(t, u, dst, wave);
+    }
+    // The u-th of this wave's copies of stage t.
+    __device__ __forceinline__ void dma_one(int t, int u, uint32_t dst, int wave) const
+    {
+        dma16(off[u], base + (int64_t)t * step, dst + (uint32_t)(wave + NW * u) * 1024u);
     }
 
     // Partial last stage: masked register loads into the same LDS positions.
-    // krel_end = valid K elements in this stage (1 .. 63).
+    // krel_end = valid K elements in this stage (1 .. BKS - 1).
     __device__ __forceinline__ void tail(int t, int krel_end, char *dst, int wave, int lane) const
     {
         const char *b = base + (int64_t)t * step;
@@ -177,20 +213,22 @@ struct Dma3 {
             const int P = pos(wave, lane, u);
             int kp;  // K offset of this lane's chunk within the stage
             if constexpr (!MN)
-                kp = 8 * ((P & 7) ^ kc3_swz(P >> 3));
+                kp = 8 * ((P % KCH) ^ kc3_swz<KCH, SW>(P / KCH));
             else
                 kp = P / CH;
             const u32x4 v = kp < krel_end ? *(const u32x4 *)(b + off[u]) : zero4();
-            *(u32x4 *)(dst + (wave + 4 * u) * 1024 + lane * 16) = v;
+            *(u32x4 *)(dst + (wave + NW * u) * 1024 + lane * 16) = v;
         }
     }
 };
 
-// K-contiguous fragment: rows r0 .. r0+15, K block kb (0 or 1) of the stage.
+// K-contiguous fragment: rows r0 .. r0+15, 32-deep K block kb of the stage
+// (rows of KCH chunks).
+template <int KCH = 8>
 __device__ __forceinline__ u32x4 frag3_kc(const char *st, int r0, int kb, int lane)
 {
     const int r = r0 + (lane & 15), g = lane >> 4;
-    return *(const u32x4 *)(st + r * 128 + 16 * ((4 * kb + g) ^ kc3_swz(r)));
+    return *(const u32x4 *)(st + r * (KCH * 16) + 16 * ((4 * kb + g) ^ kc3_swz<KCH>(r)));
 }
 
 // M/N-contiguous fragment: two transposed 64-bit reads give 8 k values of
@@ -228,17 +266,18 @@ __device__ __forceinline__ u32x4 frag3_mn(uint32_t b0, uint32_t b1, int n0)
     return out;
 }
 
-template <typename Tr, int BM, int BN, int S, bool TA, bool TB>
-__global__ __launch_bounds__(256) void mfma_gemm3_kernel(MfmaArgs p)
+template <typename Tr, int BM, int BN, int S, int WGM, int WGN, bool TA, bool TB>
+__global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
 {
     // The LDS-DMA and transposed-read builtins exist on the device side only;
     // the host pass needs nothing but the signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = typename Tr::T;
-    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int NW = WGM * WGN;                         // waves per workgroup
+    constexpr int WM = BM / WGM, WN = BN / WGN;           // wave sub-tile
     constexpr int FM = WM / 16, FN = WN / 16;
-    using OpA = Dma3<BM, TA>;
-    using OpB = Dma3<BN, !TB>;
+    using OpA = Dma3<BM, TA, NW>;
+    using OpB = Dma3<BN, !TB, NW>;
     constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int NDMA = OpA::PER_WAVE + OpB::PER_WAVE;  // copies per wave per stage
@@ -250,7 +289,7 @@ __global__ __launch_bounds__(256) void mfma_gemm3_kernel(MfmaArgs p)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
 
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
@@ -363,11 +402,15 @@ __global__ __launch_bounds__(256) void mfma_gemm3_kernel(MfmaArgs p)
         // refill of fa[i] with the next block's fragment, and each of the first
         // HALF rows also by a share of the next block's B fragments (into nb).
         // When the next block starts stage t + 1, the wave synchronises after
-        // its first row of MFMAs.
+        // its first row of MFMAs, and the copies of stage t + S into the buffer
+        // just released are spread one per row over the rest of the block, so
+        // the matrix unit is never left waiting behind a burst of copy issues.
         auto body = [&](int t, int kb, const u32x4 *fb, u32x4 *nb, bool more) {
             const int tn1 = kb ? t + 1 : t;        // stage of the next block
             const int kbn = kb ? 0 : 1;
             const char *nst_p = lds + (tn1 % S) * STAGE;
+            const bool refill = more && kb == 1 && t + S < nst;
+            const uint32_t rslot = lds_base + ((t + S) % S) * STAGE;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -378,8 +421,18 @@ __global__ __launch_bounds__(256) void mfma_gemm3_kernel(MfmaArgs p)
                         // stages up to t + S - 1 have been issued
                         wait_stage(t + 1, min(nst - 1, t + S - 1));
                         lds_barrier();
-                        if (t + S < nst)
-                            issue(t + S);
+                    }
+                    if (kb == 1) {
+                        // copies q = i, i + FM, ... of stage t + S (DMA: t + S >= 1)
+#pragma unroll
+                        for (int q = i; q < NDMA; q += FM) {
+                            if (refill) {
+                                if (q < OpA::PER_WAVE)
+                                    oa.dma_one(t + S - has_tail, q, rslot, wave);
+                                else
+                                    ob.dma_one(t + S - has_tail, q - OpA::PER_WAVE, rslot + A_BYTES, wave);
+                            }
+                        }
                     }
                     if (i < HALF) {
 #pragma unroll
@@ -388,6 +441,8 @@ __global__ __launch_bounds__(256) void mfma_gemm3_kernel(MfmaArgs p)
                     }
                     fa[i] = read_a(nst_p, kbn, i);
                 }
+                // keep each row's MFMAs and reads where they are
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
         // Two K blocks (one stage) per trip; the B fragments ping-pong between
