@@ -37,6 +37,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["tiled_gemm_02_amd/csrc/kernels/common.hpp",
                   "tiled_gemm_02_amd/csrc/kernels/mfma_gemm.hpp",
                   "tiled_gemm_02_amd/csrc/kernels/mfma_gemm3.hpp",
+                  "tiled_gemm_02_amd/csrc/kernels/mfma_pingpong.hpp",
+                  "tiled_gemm_02_amd/csrc/kernels/instances.inc",
                   "tiled_gemm_02_amd/csrc/kernels/gemv.hpp",
                   "tiled_gemm_02_amd/csrc/kernels/skinny.hpp",
                   "tiled_gemm_02_amd/csrc/kernels/aux_kernels.hpp"]
@@ -105,11 +107,18 @@ def time_workload(name: str, steps: int, warmup: int, device, rotate: bool):
     p = d["p"]
     epi = (tg.TG_EPI_LEAKY_RELU, d["slope"]) if d["epi"] else None
     stream = torch.cuda.current_stream(device)
+    # split-K partials: one workspace for the whole run, as a caller that
+    # cares about throughput passes it (without it the library makes a
+    # stream-ordered allocation per call)
+    plan0 = tg.plan_for(d["As"][0], d["Bs"][0], trans_a=p.trans_a, trans_b=p.trans_b)
+    ws = None
+    if plan0["workspace_bytes"] > 0:
+        ws = torch.empty(int(plan0["workspace_bytes"]), dtype=torch.uint8, device=device)
 
     def step(i):
         j = i % d["copies"]
         tg.gemm(d["As"][j], d["Bs"][j], trans_a=p.trans_a, trans_b=p.trans_b, epilogue=epi,
-                out=d["C"], stream=stream.cuda_stream)
+                out=d["C"], workspace=ws, stream=stream.cuda_stream)
 
     for i in range(warmup):
         step(i)

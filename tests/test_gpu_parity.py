@@ -189,7 +189,7 @@ def test_split_k_caller_workspace():
 @pytest.mark.parametrize("dtype", [F16, BF16])
 @pytest.mark.parametrize("trans", [NN, NT])
 @pytest.mark.parametrize("shape", [(128, 128, 256), (200, 64, 264), (1000, 120, 1000), (136, 8, 512),
-                                   (4096, 128, 2048)])
+                                   (584, 72, 1096), (4096, 128, 2048)])
 def test_skinny(dtype, trans, shape):
     import tiled_gemm_02_amd as tg
     M, N, K = shape

@@ -333,6 +333,8 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         kps = (kps + BK - 1) / BK * BK;
         a.kps = (int)kps;
         a.splits = pl.split_k;
+        a.nrb = (int)((p.M + kSkRows - 1) / kSkRows);
+        a.skew = kSkinnySkew;
         a.epi = epi_kind;
         a.slope = slope;
         const int cb = elem_bytes(p.dtype);

@@ -4,23 +4,39 @@
 // Multiplication Background User's Guide", section 2, works this example),
 // below MI355X's ~315 FLOP/byte ridge, so the time is the time to stream A
 // from HBM once.  A still needs the matrix cores: at 8 TB/s the multiply-adds
-// arrive faster than the vector ALUs retire them.  The kernel is therefore an
-// HBM stream that feeds MFMAs:
-//   * a workgroup owns 64 rows of C and all (<= 128) of its columns, over a
-//     K range (split K across workgroups when M alone gives too few of them);
-//   * A goes straight from HBM into MFMA operand registers (each lane loads
-//     16 bytes of one row), prefetched two K steps ahead - it is used once,
-//     so staging it through LDS would only add traffic;
-//   * B (small, L2-resident) is staged per 256-deep K step into LDS as
-//     K-contiguous rows (transposed 8 x 8 in registers when B is stored
-//     N-contiguous), XOR-swizzled so both the writes and the fragment reads
-//     are bank-conflict free, double buffered;
-//   * the 8 waves split each K step four ways (and the 64 rows two ways), so
-//     LDS traffic per byte of A stays low; their partial tiles are summed in
-//     LDS in a fixed order ((w0 + w2) + (w1 + w3)) before the epilogue.
+// arrive faster than the vector ALUs retire them.  The kernel is an HBM stream
+// that feeds MFMAs, shaped by what the memory system rewards:
+//   * every CU streams its own slice of A: a CU keeps only a bounded number of
+//     cache lines in flight, so the full rate needs all 256 CUs reading
+//     distinct data (two workgroups reading the same lines each wait a full
+//     HBM round trip); a workgroup owns 64 rows of C and all of its columns
+//     (64 or 128), and K is split across workgroups when the row blocks alone
+//     leave CUs idle;
+//   * B (small, L2-resident) is re-read by every row block; its lines come
+//     from L2 with a short round trip;
+//   * A and B move into LDS by buffer loads that write LDS directly
+//     (buffer_load ... lds) in 64-deep K stages.  The two operands have rings
+//     of their own: A, whose lines take an HBM round trip, keeps 9 to 13
+//     stages in flight; B keeps 3.  Each copy instruction covers 1 KiB (8 rows
+//     x 128 contiguous bytes of A).  The buffer bound turns rows past M,
+//     columns past N and K past the range into zeros with no branch and no
+//     tail path;
+//   * one wave sustains only a few GB/s of such copies and its waits are in
+//     issue order, so a 16-wave workgroup gives A and B separate copy waves
+//     (8 each); four of the B waves also run the MFMAs (2 x 2 grid, each
+//     32 rows x CN/2 columns of v_mfma_f32_16x16x32, fp32 accumulate);
+//   * row blocks start their K sweep at different stages, which spreads the
+//     concurrent requests over the memory channels (rows of A are a power of
+//     two apart, so requests for one K offset crowd the same channels);
+//   * LDS layouts are swizzled for gfx950's banks: A (and B stored N x K) as
+//     K-contiguous rows of 8 chunks, B stored K x N as M/N-contiguous k-rows
+//     read back transposed (ds_read_b64_tr_b16).
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
+#include "mfma_gemm3.hpp"
 
 namespace tg {
 
@@ -31,246 +47,284 @@ struct SkinnyArgs {
     float *ws;       // split partials [splits][M][N]
     int64_t lda, ldb, ldc;
     int M, N, K;
-    int kps;         // K per split, multiple of 256
+    int kps;         // K per split (multiple of kSkBK)
     int splits;
+    int nrb;         // row blocks, ceil(M / kSkRows)
+    int skew;        // stages between the start points of consecutive XCDs
     int epi;
     float slope;
     int c_vec;
 };
 
 constexpr int kSkRows = 64;     // C rows per workgroup
-constexpr int kSkCols = 128;    // C columns covered (N <= 128)
-constexpr int kSkBK = 256;      // K per step
-constexpr int kSkChunks = kSkBK / 8;  // 16-byte chunks per LDS row (32)
+constexpr int kSkBK = 64;       // K per stage
+constexpr int kSkLds = 144 * 1024;   // LDS of the two rings
+constexpr int kSkStagesB = 4;        // B ring stages (A gets the rest)
 
-__device__ __forceinline__ int sk_swz(int n) { return (n ^ (n >> 3)) & 15; }
-
-template <typename Tr, bool TB>
-__global__ __launch_bounds__(512) void skinny_kernel(SkinnyArgs p)
+// Raw buffer resource over [base, base + bytes): offsets at or past `bytes`
+// read as zeros.  Word 3 is the gfx9 raw-buffer format.
+__device__ __forceinline__ u32x4 sk_rsrc(const void *base, uint32_t bytes)
 {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// One 16-byte-per-lane buffer load written straight into LDS at m0 + 16 lane.
+// Its completion is counted by vmcnt; the compiler does not see it as a
+// memory operation, so the waits are the caller's.
+__device__ __forceinline__ void sk_copy(const u32x4 &rs, uint32_t voff, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(rs)
+                 : "memory", "m0");
+}
+
+// s_waitcnt leaving the copies of the y youngest stages (ND per stage) in
+// flight, y <= Y.
+template <int ND, int Y>
+__device__ __forceinline__ void sk_wait_younger(int y)
+{
+    if constexpr (Y > 0) {
+        if (y >= Y) {
+            wait_vm_lgkm<Y * ND>();
+            return;
+        }
+        sk_wait_younger<ND, Y - 1>(y);
+    } else {
+        wait_vm_lgkm<0>();
+    }
+}
+
+template <typename Tr, bool TB, int CN>
+__global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
     using T = typename Tr::T;
-    constexpr int STAGE = kSkCols * kSkChunks;  // chunks per LDS stage (64 KiB)
-    __shared__ u32x4 lds[2 * STAGE];
+    constexpr int BK = kSkBK;
+    constexpr int KS = BK / 32;                           // MFMA K steps per stage
+    constexpr int WR = 2, WC = 2;                         // compute waves: a 2 x 2 grid
+    constexpr int MB = kSkRows / 16 / WR, NBK = CN / 16 / WC;   // 16 x 16 blocks per compute wave
+    constexpr int A_BYTES = kSkRows * BK * 2;             // 8 KiB: 8 copies of 1 KiB
+    constexpr int B_BYTES = CN * BK * 2;                  // 8 or 16 KiB
+    constexpr int SB = kSkStagesB;                        // B ring
+    constexpr int SA = (kSkLds - SB * B_BYTES) / A_BYTES; // A ring: the rest of LDS
+    constexpr int NBW = 8, NAW = 8;                       // B-copy waves 0..7, A-copy waves 8..15
+    constexpr int NBC = B_BYTES / 1024 / NBW;             // B copies per B wave per stage
+    constexpr int BCH = CN / 8;                           // chunks per k-row of B stored K x N
+    constexpr uint32_t kOut = 0x80000000u;                // past every bound (bounds < 2^31)
+    static_assert(NBC >= 1 && SA >= 3 && SB >= 2 && SA - 2 < 64, "rings");
+    __shared__ __attribute__((aligned(1024))) char lds[SA * A_BYTES + SB * B_BYTES];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int rg = wave & 1;   // row group: rows 32*rg .. 32*rg+31
-    const int kg = wave >> 1;  // K group: k 64*kg .. 64*kg+63 of each step
-    const int fr = lane & 15, g = lane >> 4;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int fr = lane & 15, fg = lane >> 4;
 
-    const int row0 = blockIdx.x * kSkRows;
+    const int rb = blockIdx.x;
+    const int row0 = rb * kSkRows;
     const int z = blockIdx.y;
     const int kbeg = z * p.kps;
     const int kend = min(p.K, kbeg + p.kps);
-    const int nsteps = (kend - kbeg + kSkBK - 1) / kSkBK;
+    const int nst = max(0, (kend - kbeg + BK - 1) / BK);
+    // start stage: row blocks rb and rb + 8 share an XCD (ids go round-robin
+    // over the 8 XCDs); XCDs start skew stages apart, row blocks within one
+    // XCD one stage apart
+    const int s0 = nst > 0 ? (int)(((int64_t)(rb & 7) * p.skew + (rb >> 3)) % nst) : 0;
 
     const T *A = (const T *)p.A;
     const T *B = (const T *)p.B;
+    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+    const uint32_t ldsB = lds_base + SA * A_BYTES;
 
-    // A operand rows of this lane (clamped at the bottom edge; never stored)
-    const T *arow[2];
+    // K offset of stage t: row blocks start their sweep at stage s0
+    auto stage_k0 = [&](int t) {
+        int ts = t + s0;
+        ts = ts >= nst ? ts - nst : ts;
+        return kbeg + ts * BK;
+    };
+
+    // A copy (waves 8..15, one per stage): A rows 8c .. 8c + 7 (c = wave - 8),
+    // 128 bytes each; lane l stores chunk l % 8 of row 8c + l / 8, i.e. logical
+    // chunk (l % 8) ^ swz(row), into bytes [1024 c, + 1024) of the stage.
+    // B copy u of wave w (0..7): copy j = w + 8 u of the stage's B tile.  Stored
+    // N x K, like A (rows are columns); stored K x N, k-rows of BCH chunks, lane
+    // l storing chunk l % BCH of k-row (64 / BCH) j + l / BCH.
+    // Per lane: the byte offset at K offset 0 and the stage-relative K it reads.
+    uint32_t c_off[NBC];
+    int c_k[NBC];
+    u32x4 rs;
+    if (wave >= NBW) {
+        const int c = wave - NBW;
+        const int rows_here = min(kSkRows, p.M - row0);
+        rs = sk_rsrc(A + (int64_t)row0 * p.lda, (uint32_t)((int64_t)rows_here * p.lda * 2));
+        const int r = 8 * c + (lane >> 3);
+        const int lc = (lane & 7) ^ kc3_swz<8>(r);
+        c_k[0] = 8 * lc;
+        c_off[0] = (uint32_t)(r * p.lda * 2 + 16 * lc);
+    } else {
+        rs = TB ? sk_rsrc(B, (uint32_t)((int64_t)p.N * p.ldb * 2)) : sk_rsrc(B, (uint32_t)((int64_t)p.K * p.ldb * 2));
 #pragma unroll
-    for (int fm = 0; fm < 2; ++fm) {
-        const int r = min(row0 + 32 * rg + 16 * fm + fr, p.M - 1);
-        arow[fm] = A + (int64_t)r * p.lda;
+        for (int u = 0; u < NBC; ++u) {
+            const int j = wave + NBW * u;
+            if constexpr (TB) {
+                const int n = 8 * j + (lane >> 3);
+                const int lc = (lane & 7) ^ kc3_swz<8>(n);
+                c_k[u] = 8 * lc;
+                c_off[u] = n < p.N ? (uint32_t)(n * p.ldb * 2 + 16 * lc) : kOut;
+            } else {
+                const int k = (64 / BCH) * j + lane / BCH;
+                const int n = 8 * ((lane % BCH) ^ mn3_swz<BCH>(k));
+                c_k[u] = k;
+                c_off[u] = n < p.N ? (uint32_t)(k * p.ldb * 2 + n * 2) : kOut;
+            }
+        }
     }
-    auto load_a = [&](u32x4 *dst, int k0) {
-#pragma unroll
-        for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int k = k0 + 64 * kg + 32 * kb + 8 * g;
-                dst[fm * 2 + kb] = k < kend ? *(const u32x4 *)(arow[fm] + k) : zero4();
-            }
+    auto issue_a = [&](int t) {
+        const int k0 = stage_k0(t);
+        const uint32_t off = c_k[0] < kend - k0 ? c_off[0] + 2u * (uint32_t)k0 : kOut;
+        sk_copy(rs, off, lds_base + (uint32_t)((t % SA) * A_BYTES + (wave - NBW) * 1024));
     };
-
-    // B staging: 128 columns x 256 k per step, 512 threads
-    u32x4 breg[8];
-    auto load_b = [&](int k0) {
-        if constexpr (!TB) {
-            // B stored K x N (N contiguous): one 8 x 8 block per thread
-            const int nb = tid & 15, kb8 = tid >> 4;
-            const int gc = min(8 * nb, p.N - 8);
+    auto issue_b = [&](int t) {
+        const int k0 = stage_k0(t);
+        const uint32_t step = TB ? 2u * (uint32_t)k0 : (uint32_t)((int64_t)k0 * p.ldb * 2);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int k = k0 + 8 * kb8 + e;
-                breg[e] = k < kend ? *(const u32x4 *)(B + (int64_t)k * p.ldb + gc) : zero4();
-            }
-        } else {
-            // B stored N x K (K contiguous): 8 chunks per thread
-            const int c = tid & 31;
-            const int k = k0 + 8 * c;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int n = min((tid >> 5) + 16 * q, p.N - 1);
-                breg[q] = k < kend ? *(const u32x4 *)(B + (int64_t)n * p.ldb + k) : zero4();
-            }
-        }
-    };
-    auto store_b = [&](u32x4 *dst) {
-        if constexpr (!TB) {
-            const int nb = tid & 15, kb8 = tid >> 4;
-            u32x4 t[8];
-            transpose_block<2>(breg, t);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int n = 8 * nb + j;
-                dst[n * kSkChunks + (kb8 ^ sk_swz(n))] = t[j];
-            }
-        } else {
-            const int c = tid & 31;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int n = (tid >> 5) + 16 * q;
-                dst[n * kSkChunks + (c ^ sk_swz(n))] = breg[q];
-            }
+        for (int u = 0; u < NBC; ++u) {
+            const uint32_t off = (c_k[u] < kend - k0 && c_off[u] != kOut) ? c_off[u] + step : kOut;
+            sk_copy(rs, off, ldsB + (uint32_t)((t % SB) * B_BYTES + (wave + NBW * u) * 1024));
         }
     };
 
-    f32x4 acc[2][8];
+    const int wr = (wave >> 1) & 1, wc = wave & 1;
+    uint32_t mnb[KS][2];
+    if constexpr (!TB) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+            for (int h = 0; h < 2; ++h)
+                mnb[ks][h] = mn3_base<BCH>(ldsB, ks, h, lane);
+    }
+
+    f32x4 acc[MB][NBK];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBK; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const u32x4 *a, const u32x4 *bs) {
+    // One straight-line loop per role (a role branch inside the loop would
+    // make the compiler move the accumulators out of AGPRs every iteration).
+    // Every role meets the same barrier once per stage: after it, stage t of
+    // both rings has landed and every read of stage t - 1 is done, so the
+    // slots of stage t - 1 are refilled.  A waves keep SA - 1 stages in flight
+    // (HBM latency), B waves SB - 1 (L2 latency); each wave's vmcnt counts its
+    // own copies only.
+    if (wave >= NBW) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int c = 8 * kg + 4 * kb + g;
-            u32x4 bf[8];
+        for (int t = 0; t < SA - 1; ++t)
+            if (t < nst)
+                issue_a(t);
+        for (int t = 0; t < nst; ++t) {
+            sk_wait_younger<1, SA - 2>(min(nst - 1, t + SA - 2) - t);
+            lds_barrier();
+            if (t + SA - 1 < nst)
+                issue_a(t + SA - 1);
+        }
+        return;
+    }
+    auto b_loop = [&](auto compute) {
+        constexpr bool kCompute = decltype(compute)::value;
 #pragma unroll
-            for (int fn = 0; fn < 8; ++fn) {
-                const int n = 16 * fn + fr;
-                bf[fn] = bs[n * kSkChunks + (c ^ sk_swz(n))];
+        for (int t = 0; t < SB - 1; ++t)
+            if (t < nst)
+                issue_b(t);
+        for (int t = 0; t < nst; ++t) {
+            sk_wait_younger<NBC, SB - 2>(min(nst - 1, t + SB - 2) - t);
+            lds_barrier();
+            if (t + SB - 1 < nst)
+                issue_b(t + SB - 1);
+            if constexpr (kCompute) {
+                const char *sa = lds + (t % SA) * A_BYTES;
+                const char *sb = lds + SA * A_BYTES + (t % SB) * B_BYTES;
+                const uint32_t so = (uint32_t)((t % SB) * B_BYTES);
+                u32x4 fa[KS][MB], fb[KS][NBK];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int x = 0; x < MB; ++x)
+                        fa[ks][x] = frag3_kc<8>(sa, 16 * (MB * wr + x), ks, lane);
+#pragma unroll
+                    for (int x = 0; x < NBK; ++x) {
+                        if constexpr (TB)
+                            fb[ks][x] = frag3_kc<8>(sb, 16 * (NBK * wc + x), ks, lane);
+                        else
+                            fb[ks][x] = frag3_mn<BCH>(mnb[ks][0] + so, mnb[ks][1] + so, 16 * (NBK * wc + x));
+                    }
+                }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int i = 0; i < MB; ++i)
+#pragma unroll
+                        for (int j = 0; j < NBK; ++j)
+                            mfma_tied<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
             }
-#pragma unroll
-            for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < 8; ++fn)
-                    mfma_chunk<Tr>(acc[fm][fn], bf[fn], a[fm * 2 + kb]);
         }
     };
-
-    if (nsteps > 0) {
-        // A is prefetched two steps ahead in a 3-slot ring
-        u32x4 abuf[3][4];
-        load_b(kbeg);
-        load_a(abuf[0], kbeg);
-        if (nsteps > 1)
-            load_a(abuf[1], kbeg + kSkBK);
-        store_b(lds);
-        __syncthreads();
-
-        auto body = [&](int t, u32x4 *acur, u32x4 *afar) {
-            const bool more = t + 1 < nsteps;
-            if (more)
-                load_b(kbeg + (t + 1) * kSkBK);
-            if (t + 2 < nsteps)
-                load_a(afar, kbeg + (t + 2) * kSkBK);
-            compute(acur, lds + (t & 1) * STAGE);
-            if (more)
-                store_b(lds + ((t + 1) & 1) * STAGE);
-            __syncthreads();
-        };
-        for (int t = 0; t < nsteps; t += 3) {
-            body(t, abuf[0], abuf[2]);
-            if (t + 1 < nsteps)
-                body(t + 1, abuf[1], abuf[0]);
-            if (t + 2 < nsteps)
-                body(t + 2, abuf[2], abuf[1]);
-        }
-    }
-
-    // ---- sum the four K groups: (kg0 + kg2) + (kg1 + kg3), per row group
-    float *red = (float *)lds;  // [4 waves][64 values][64 lanes]
-    if (kg >= 2) {
-        float *dst = red + ((kg - 2) * 2 + rg) * 64 * 64;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dst[((i * 8 + j) * 4 + e) * 64 + lane] = acc[i][j][e];
-    }
-    __syncthreads();
-    if (kg < 2) {
-        const float *src = red + (kg * 2 + rg) * 64 * 64;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc[i][j][e] += src[((i * 8 + j) * 4 + e) * 64 + lane];
-    }
-    __syncthreads();
-    if (kg == 1) {
-        float *dst = red + rg * 64 * 64;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dst[((i * 8 + j) * 4 + e) * 64 + lane] = acc[i][j][e];
-    }
-    __syncthreads();
-    if (kg != 0)
+    if (wave >= WR * WC) {
+        b_loop(std::false_type{});
         return;
-    {
-        const float *src = red + rg * 64 * 64;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc[i][j][e] += src[((i * 8 + j) * 4 + e) * 64 + lane];
     }
+    b_loop(std::true_type{});
+    mfma_drain();
 
-    // ---- epilogue: lane holds C[m][n .. n+3]
+    // ---- epilogue: lane holds C[m][n .. n + 3] of each of its blocks
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int m = row0 + 32 * rg + 16 * i + fr;
+    for (int i = 0; i < MB; ++i) {
+        const int m = row0 + 16 * (MB * wr + i) + fr;
         if (m >= p.M)
             continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int n = 16 * j + 4 * g;
-            if (n >= p.N)
+        for (int j = 0; j < NBK; ++j) {
+            const int ncol = 16 * (NBK * wc + j) + 4 * fg;
+            if (ncol >= p.N)
                 continue;
+            const f32x4 s = acc[i][j];
             if (p.splits > 1) {
-                float *dst = p.ws + ((int64_t)z * p.M + m) * p.N + n;
-                if (n + 3 < p.N && (p.N & 3) == 0) {
-                    *(f32x4 *)dst = acc[i][j];
-                } else {
+                float *dst = p.ws + ((int64_t)z * p.M + m) * p.N + ncol;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < p.N)
-                            dst[e] = acc[i][j][e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (ncol + e < p.N)
+                        dst[e] = s[e];
                 continue;
             }
             T v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v[e] = Tr::from_f32(apply_epi(acc[i][j][e], p.epi, p.slope));
-            T *dst = (T *)p.C + (int64_t)m * p.ldc + n;
-            if (p.c_vec && n + 3 < p.N) {
+                v[e] = Tr::from_f32(apply_epi(s[e], p.epi, p.slope));
+            T *dst = (T *)p.C + (int64_t)m * p.ldc + ncol;
+            if (p.c_vec && ncol + 3 < p.N) {
                 u32x2 w;
-                w[0] = __builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
-                w[1] = __builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
+                w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
+                w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
                 *(u32x2 *)dst = w;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (n + e < p.N)
+                    if (ncol + e < p.N)
                         dst[e] = v[e];
             }
         }
     }
+#else
+    (void)p;
+#endif
 }
 
 }  // namespace tg

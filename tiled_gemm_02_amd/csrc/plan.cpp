@@ -338,8 +338,13 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
 
 static bool skinny_fits(const Problem &p)
 {
+    // buffer offsets are 32-bit with bit 31 reserved as "out of range": one
+    // 64-row block of A, and all of B, must span less than 2^31 bytes
+    const int64_t lim = (int64_t)1 << 31;
+    const bool tb = (p.trans & TG_TRANS_B) != 0;
+    const bool fit32 = (int64_t)kSkinnyRows * p.lda * 2 < lim && (tb ? p.N : p.K) * p.ldb * 2 < lim;
     return p.dtype != TG_F32 && p.N <= kSkinnyMaxN && p.N >= 8 && p.M >= 2 * kSkinnyRows &&
-           vec_ok(p) && !(p.trans & TG_TRANS_A);
+           vec_ok(p) && !(p.trans & TG_TRANS_A) && fit32;
 }
 
 static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opts, tg_plan *out,
@@ -351,17 +356,18 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
     }
     if (!skinny_fits(p)) {
         *why = "skinny path needs 16-bit operands, A not transposed, 8 <= N <= 128, M >= 128, "
-               "dimensions and leading dimensions multiples of 8, 16-byte aligned";
+               "dimensions and leading dimensions multiples of 8, 16-byte aligned, and operand "
+               "spans below 2 GiB";
         return TG_ERR_UNSUPPORTED;
     }
     const int BK = kSkinnyBK;
     const int64_t tm = (p.M + kSkinnyRows - 1) / kSkinnyRows;
-    // split K until the grid covers every CU about twice, one BK step per split at least
+    // split K until every CU streams its own part of A, four stages per split at least
     int s = 1;
     if (opts && opts->split_k > 0) {
         s = opts->split_k;
     } else {
-        while (tm * s < (int64_t)chip.num_cus && (int64_t)(s * 2) * 2 * BK <= p.K && s < 16)
+        while (tm * s < (int64_t)chip.num_cus && (int64_t)(s * 2) * 4 * BK <= p.K && s < 16)
             s *= 2;
     }
     int64_t kps = (p.K + s - 1) / s;
@@ -369,7 +375,7 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
     s = (int)((p.K + kps - 1) / kps);
     out->path = TG_PATH_SKINNY;
     out->tile_m = kSkinnyRows;
-    out->tile_n = kSkinnyMaxN;
+    out->tile_n = p.N > 64 ? 128 : 64;
     out->tile_k = BK;
     out->split_k = s;
     out->occupancy = 1;
@@ -378,7 +384,7 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
     out->workgroups = tm * s;
     const int64_t slots = (int64_t)chip.num_cus * out->occupancy;
     out->waves = (out->workgroups + slots - 1) / slots;
-    out->tile_eff = (double)p.N / kSkinnyMaxN * (double)p.M / (tm * kSkinnyRows);
+    out->tile_eff = (double)p.N / out->tile_n * (double)p.M / (tm * kSkinnyRows);
     out->wave_eff = (double)out->workgroups / (double)(out->waves * slots);
     out->workspace_bytes = s > 1 ? (uint64_t)s * p.M * p.N * 4u : 0;
     const double bytes = alg_bytes(p) + 2.0 * (double)out->workspace_bytes;

@@ -46,10 +46,12 @@ bool has_mfma_tile(int dtype, int bm, int bn, bool vec);
 // limited by LDS (160 KiB per CU) and the kernels' register use.
 int model_occupancy(int dtype, int bm, int bn, bool vec);
 
-// Skinny kernel geometry (N <= kSkinnyMaxN).
-constexpr int kSkinnyRows = 64;    // output rows per workgroup
-constexpr int kSkinnyMaxN = 128;   // widest output it covers in one pass
-constexpr int kSkinnyBK = 256;     // K per step
+// Skinny kernel geometry (N <= kSkinnyMaxN): a workgroup covers 64 rows and
+// all columns (64 or 128); K is split until the row blocks fill the CUs.
+constexpr int kSkinnyRows = 64;        // output rows per workgroup
+constexpr int kSkinnyMaxN = 128;       // widest output it covers in one pass
+constexpr int kSkinnyBK = 64;          // K per pipeline stage, the granularity of a split
+constexpr int kSkinnySkew = 16;        // stages between the K start points of consecutive XCDs
 constexpr bool kSkinnyEnabled = true;
 
 // Occupancy lookup: returns workgroups per CU for a tile kernel; the device
