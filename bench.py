@@ -186,6 +186,178 @@ def roofline_entry(r, bound):
             "peak": peak, "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
+# ---------------------------------------------------------------- HBM traffic counters
+#
+# roofline.traffic comes from two rocprofv3 counter passes per workload
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) over `bench.py --traffic-kernel
+# NAME`, each scaled by what the same counter reads for a plain 256 MiB device
+# copy (`--traffic-kernel copy`).  `--traffic-summarize DIR` turns the counter
+# files into TRAFFIC_FILE, tagged with a hash of the kernel sources so that a
+# changed kernel reports null until it is measured again.
+
+TRAFFIC_WORKLOADS = ["f16_8192", "f16_skinny_8192x128x8192", "f16_gemv_1x8192x8192"]
+COPY_BYTES = 256 << 20
+DOMINANT = {"mfma": "mfma_", "skinny": "skinny_kernel"}   # GEMV: gemv_cols / gemv_rows
+
+
+def traffic_kernel(name: str, launches: int = 6):
+    """Run one workload's kernels (or the calibration copy) for a counter pass."""
+    import torch
+    device = torch.device("cuda:0")
+    if name == "copy":
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(launches):
+            dst.copy_(src)
+        torch.cuda.synchronize(device)
+        return
+    import tiled_gemm_02_amd as tg
+    from gemm_inputs import WORKLOADS
+    w = WORKLOADS[name]
+    time_workload(name, launches, 1, device, rotate=w["N"] <= 256 or w["M"] == 1)
+    del tg
+
+
+def _counter_avg(csv_path: str, sub: str, counter: str):
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if sub in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            d = int(r["Dispatch_Id"])
+            per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)[1:] if len(per) > 1 else sorted(per)   # the first dispatch runs cold
+    return (sum(per[i] for i in ids) / len(ids), len(ids)) if ids else (None, 0)
+
+
+def traffic_summarize(root: str):
+    import glob
+    import tiled_gemm_02_amd as tg
+    from gemm_inputs import ELEM_BYTES, WORKLOADS
+
+    def find(tag):
+        f = glob.glob(os.path.join(root, tag, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter file under {root}/{tag}")
+        return f[0]
+
+    cf, _ = _counter_avg(find("copy_fetch"), "copy", "FETCH_SIZE")
+    cw, _ = _counter_avg(find("copy_write"), "copy", "WRITE_SIZE")
+    k_fetch = COPY_BYTES / (cf * 1024.0)
+    k_write = COPY_BYTES / (cw * 1024.0)
+    out = {"_calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cf, "write_kib": cw,
+                            "fetch_factor": k_fetch, "write_factor": k_write}}
+    lines = ["# HBM traffic per launch of each workload's dominant kernel", "",
+             "Counters: rocprofv3 `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch, first dispatch",
+             "dropped), one pass each, scaled by the reading of the same counter for a plain",
+             f"{COPY_BYTES >> 20} MiB device copy (factors {k_fetch:.3f} fetch, {k_write:.3f} write).", "",
+             "Commands (repository root, one MI355X; NAME is each workload below, and `copy`):", "",
+             "```",
+             "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/traffic/NAME_fetch -o run --output-format csv -- python3 bench.py --traffic-kernel NAME",
+             "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/traffic/NAME_write -o run --output-format csv -- python3 bench.py --traffic-kernel NAME",
+             "python3 bench.py --traffic-summarize gpurun_out/traffic",
+             "```", "",
+             "| Workload | Kernel | Fetch (MiB) | Write (MiB) | Total (MiB) | Algorithmic (MiB) | Ratio |",
+             "|---|---|---|---|---|---|---|"]
+    for name in TRAFFIC_WORKLOADS:
+        w = WORKLOADS[name]
+        plan = tg.tg_plan_model(w["M"], w["N"], w["K"], w["dtype"], w["trans"], num_cus=256)
+        if plan["path_name"] == "gemv":
+            sub = "gemv_rows" if plan["tile_m"] == 4 else "gemv_cols"
+        else:
+            sub = DOMINANT[plan["path_name"]]
+        f, nf = _counter_avg(find(name + "_fetch"), sub, "FETCH_SIZE")
+        wr, nw = _counter_avg(find(name + "_write"), sub, "WRITE_SIZE")
+        if f is None or wr is None:
+            raise SystemExit(f"no {sub} dispatches for {name}")
+        fb, wb = f * 1024.0 * k_fetch, wr * 1024.0 * k_write
+        alg = ELEM_BYTES[w["dtype"]] * (w["M"] * w["K"] + w["K"] * w["N"] + w["M"] * w["N"])
+        out[name] = {"kernel": sub, "kernel_hash": kernel_source_hash(), "fetch_bytes": fb,
+                     "write_bytes": wb, "bytes_per_launch": fb + wb, "alg_bytes": alg,
+                     "dispatches": [nf, nw]}
+        lines.append(f"| {name} | `{sub}` | {fb / 2**20:.1f} | {wb / 2**20:.1f} | {(fb + wb) / 2**20:.1f} | "
+                     f"{alg / 2**20:.1f} | {(fb + wb) / alg:.3f} |")
+    lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", ""]
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    open(os.path.join(ROOT, "profiles", "traffic_summary.md"), "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+# ---------------------------------------------------------------- quantization sweep
+
+def sweep(out_path: str, step: int, reps: int = 5):
+    """fp16 M=2304, K=4096, N = 1536 .. 6144: the planner's tile against a fixed 256 x 256 one.
+
+    Inputs are N(0,1)/sqrt(K), seeded; each point is the median of `reps` timed calls after two
+    warm-up calls, from HIP events on the launch stream."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    from gemm_inputs import F16, NN, sweep_ns
+    device = torch.device("cuda:0")
+    M, K = 2304, 4096
+    g = torch.Generator(device=device).manual_seed(4)
+    A = (torch.randn((M, K), generator=g, device=device) / math.sqrt(K)).half()
+    Bfull = (torch.randn((K, 6144), generator=g, device=device) / math.sqrt(K)).half()
+    Cfull = torch.empty((M, 6144), dtype=torch.float16, device=device)
+    stream = torch.cuda.current_stream(device)
+    fixed = dict(path=tg.TG_PATH_MFMA, tile_m=256, tile_n=256, split_k=1)
+
+    # split-K partials go to one persistent workspace (as in the timed bench)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=device)
+
+    def timed(B, C, opts):
+        for _ in range(2):
+            tg.gemm(A, B, out=C, options=opts, workspace=ws, stream=stream.cuda_stream)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            tg.gemm(A, B, out=C, options=opts, workspace=ws, stream=stream.cuda_stream)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    rows = []
+    for N in sweep_ns(step=step):
+        B = Bfull[:, :N].contiguous()
+        C = Cfull[:, :N]
+        pl = tg.tg_gemm_plan(M, N, K, F16, NN)
+        ms = timed(B, C, None)
+        ms_f = timed(B, C, fixed)
+        fl = 2.0 * M * N * K
+        rows.append((N, pl["tile_m"], pl["tile_n"], pl["split_k"], pl["tiles"], pl["waves"],
+                     fl / ms / 1e9, fl / ms_f / 1e9, pl["pred_eff"]))
+        log(f"N={N} plan {pl['tile_m']}x{pl['tile_n']} tiles {pl['tiles']} waves {pl['waves']}: "
+            f"{rows[-1][6]:.0f} TFLOP/s (fixed 256x256: {rows[-1][7]:.0f})")
+    better = sum(1 for r in rows if r[6] >= r[7] * 0.98)
+    mean_p = sum(r[6] for r in rows) / len(rows)
+    mean_f = sum(r[7] for r in rows) / len(rows)
+    lines = ["# Tile/wave-quantization sweep: fp16 M=2304, K=4096, N = 1536 .. 6144", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"python3 bench.py --sweep {out_path} --sweep-step {step}", "```", "",
+             f"{len(rows)} points, step {step}.  Mean TFLOP/s: planner {mean_p:.0f}, fixed 256x256 "
+             f"{mean_f:.0f}; the planner is within 2 % of or above the fixed tile at {better} of "
+             f"{len(rows)} points.", "",
+             "Bands of equal plan (tile, waves of 256 CUs); TFLOP/s min / median / max within the band:", "",
+             "| N range | Tile | Split | Tiles | Waves | Planner TFLOP/s | Fixed 256x256 TFLOP/s |",
+             "|---|---|---|---|---|---|---|"]
+    i = 0
+    while i < len(rows):
+        j = i
+        while j + 1 < len(rows) and rows[j + 1][1:4] == rows[i][1:4] and rows[j + 1][5] == rows[i][5]:
+            j += 1
+        band = rows[i:j + 1]
+        def mmm(k):
+            v = sorted(r[k] for r in band)
+            return f"{v[0]:.0f} / {v[len(v) // 2]:.0f} / {v[-1]:.0f}"
+        lines.append(f"| {band[0][0]}-{band[-1][0]} | {band[0][1]}x{band[0][2]} | {band[0][3]} | "
+                     f"{band[0][4]}-{band[-1][4]} | {band[0][5]} | {mmm(6)} | {mmm(7)} |")
+        i = j + 1
+    lines.append("")
+    open(out_path, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,7 +368,17 @@ def main():
                     help="comma-separated memory-bound workloads reported alongside ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sweep", default=None,
+                    help="run the M=2304, K=4096 N-sweep, write its summary to this file, then exit")
+    ap.add_argument("--sweep-step", type=int, default=8)
+    ap.add_argument("--traffic-kernel", default=None,
+                    help="run one workload (or 'copy') for a rocprofv3 counter pass, then exit")
+    ap.add_argument("--traffic-summarize", default=None,
+                    help="turn counter passes under this folder into the traffic table, then exit")
     args = ap.parse_args()
+    if args.traffic_summarize:
+        traffic_summarize(args.traffic_summarize)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -212,6 +394,12 @@ def main():
         sys.exit(1)
     tg.load()
     device = torch.device("cuda:0")
+    if args.traffic_kernel:
+        traffic_kernel(args.traffic_kernel)
+        return
+    if args.sweep:
+        sweep(args.sweep, args.sweep_step)
+        return
     log("device", torch.cuda.get_device_name(0), "cus", tg.tg_device_cus())
 
     w = WORKLOADS[args.workload]

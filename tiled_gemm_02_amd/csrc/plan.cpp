@@ -25,9 +25,13 @@ namespace tg {
 
 // Relative per-CU efficiencies are measured values of these kernels on
 // MI355X (largest tile = 1); LDS is 2 stages x (BM + BN) rows x 128 bytes.
+// eff: the fraction of the chip's dense matrix peak one saturated CU sustains
+// with that tile's kernel, measured at 8192^3 fp16 on MI355X (256 x 256: the
+// ping-pong kernel, about 1250 TFLOP/s under the board's power limit; the
+// others: the 4-wave LDS-DMA kernel).
 static const TileSpec kTiles16[] = {
-    {256, 256, 1.00, 128}, {256, 128, 0.90, 96}, {128, 128, 0.78, 64},
-    {128, 64, 0.60, 48},   {64, 64, 0.42, 32},
+    {256, 256, 0.50, 160}, {256, 128, 0.355, 96}, {128, 128, 0.385, 64},
+    {128, 64, 0.31, 48},   {64, 64, 0.22, 32},
 };
 static const TileSpec kTiles32[] = {
     {128, 128, 1.00, 64},
@@ -231,13 +235,14 @@ static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int
     const int64_t slots = (int64_t)chip.num_cus * occ;
     c.waves = (c.units + slots - 1) / slots;
     const double t_unit = occ * (2.0 * bm * bn * (double)kps) / (flop_rate_cu(chip, p.dtype) * eff);
-    double t = c.waves * t_unit;
-    double bytes = alg_bytes(p);
+    // the tile kernel: waves of tiles, or its own HBM traffic (operands, and
+    // the float32 partials it writes when K is split), whichever is longer
+    const double partials = c.s > 1 ? (double)c.s * p.M * p.N * 4.0 : 0.0;
+    double t = std::max(c.waves * t_unit, (alg_bytes(p) + partials) / (chip.hbm_gbs * 1e9));
+    // a split adds the reduction kernel after it: partials in, C out
     if (c.s > 1)
-        bytes += 2.0 * c.s * (double)p.M * p.N * 4.0;
-    t = std::max(t, bytes / (chip.hbm_gbs * 1e9));
-    if (c.s > 1)
-        t += chip.launch_us * 1e-6;
+        t += (partials + (double)p.M * p.N * elem_bytes(p.dtype)) / (chip.reduce_gbs * 1e9) +
+             chip.launch_us * 1e-6;
     c.t = t;
     return c;
 }

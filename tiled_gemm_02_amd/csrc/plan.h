@@ -17,7 +17,8 @@ struct Chip {
     double mfma32_flop_clk = 256;   // fp32 matrix-core FLOP per clock per CU
     double valu_flop_clk = 256;     // fp32 vector FMA FLOP per clock per CU
     double hbm_gbs = 8000.0;      // HBM3E bandwidth, GB/s
-    double launch_us = 2.0;       // cost charged per extra kernel launch
+    double launch_us = 3.0;       // cost charged per extra kernel launch
+    double reduce_gbs = 2500.0;   // streaming rate of the split-K reduction kernel
 };
 
 // Everything the planner may look at for one call.
@@ -35,7 +36,7 @@ struct Problem {
 // one tile only.
 struct TileSpec {
     int bm, bn;
-    double eff;      // relative throughput of a saturated CU
+    double eff;      // fraction of the dense matrix peak a saturated CU sustains
     int lds_kib;     // LDS per workgroup (2 stages)
 };
 
