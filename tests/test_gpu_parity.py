@@ -184,6 +184,28 @@ def test_split_k_caller_workspace():
     assert r["ok"], r
 
 
+@pytest.mark.parametrize("case", ["gemv", "skinny"])
+def test_split_partials_ignore_stale_workspace(case):
+    """K-split partials are fully rewritten by every call: arbitrary bytes left
+    in a reused workspace must not change the result."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    if case == "gemv":
+        M, N, K, opts = 1, 4096, 8192, None
+    else:
+        M, N, K, opts = 1024, 128, 4096, dict(path=tg.TG_PATH_SKINNY, split_k=4)
+    p = make_problem(M, N, K, F16, NN, "uniform", seed=12)
+    pl = tg.tg_gemm_plan(M, N, K, F16, NN, opts)
+    assert pl["split_k"] > 1
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    ws = torch.randint(0, 256, (pl["workspace_bytes"],), dtype=torch.uint8, device="cuda:0", generator=g)
+    for fill in (None, 0xFF, None):
+        if fill is not None:
+            ws.fill_(fill)
+        r, _, _ = check_full(p, options=opts, workspace=ws)
+        assert r["ok"], (case, fill, r)
+
+
 # ---------------------------------------------------------------- skinny path
 
 @pytest.mark.parametrize("dtype", [F16, BF16])

@@ -26,19 +26,32 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
         const float *src = ws + (int64_t)m * N + n;
         float s[4] = {0.f, 0.f, 0.f, 0.f};
         const bool vec_in = (N & 3) == 0;
-        for (int z = 0; z < splits; ++z) {
-            const float *q = src + (int64_t)z * plane;
-            if (vec_in) {
-                const f32x4 v = *(const f32x4 *)q;
+        // four splits per round: their loads are in flight together, the sum
+        // still runs in increasing split order
+        for (int z0 = 0; z0 < splits; z0 += 4) {
+            f32x4 v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s[e] += v[e];
-            } else {
+            for (int u = 0; u < 4; ++u) {
+                v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (z0 + u < splits) {
+                    const float *q = src + (int64_t)(z0 + u) * plane;
+                    if (vec_in) {
+                        v[u] = *(const f32x4 *)q;
+                    } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < N)
-                        s[e] += q[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N)
+                                v[u][e] = q[e];
+                    }
+                }
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (z0 + u < splits) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        s[e] += v[u][e];
+                }
         }
         T *dst = C + (int64_t)m * ldc + n;
         T v[4];

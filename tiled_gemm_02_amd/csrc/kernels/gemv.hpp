@@ -219,19 +219,18 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(GemvArgs p)
         return;
     const float *w = p.ws + j;
     float s = 0.f;
-    int z = 0;
-    // eight independent loads in flight, summed in increasing z
-    for (; z + 8 <= p.ksplit; z += 8) {
-        float v[8];
+    // sixteen splits per round: their loads are in flight together, the sum
+    // still runs in increasing z
+    for (int z0 = 0; z0 < p.ksplit; z0 += 16) {
+        float v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = w[(int64_t)(z + u) * p.n];
+        for (int u = 0; u < 16; ++u)
+            v[u] = z0 + u < p.ksplit ? w[(int64_t)(z0 + u) * p.n] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            s += v[u];
+        for (int u = 0; u < 16; ++u)
+            if (z0 + u < p.ksplit)
+                s += v[u];
     }
-    for (; z < p.ksplit; ++z)
-        s += w[(int64_t)z * p.n];
     ((T *)p.O)[(int64_t)j * p.os] = Tr::from_f32(apply_epi(s, p.epi, p.slope));
 }
 
