@@ -85,6 +85,8 @@ def prepare(name: str, device, rotate: bool):
     w = dict(WORKLOADS[name])
     epi = w.pop("epilogue", None)
     slope = w.pop("slope", 0.01)
+    alpha = w.pop("alpha", 1.0)
+    beta = w.pop("beta", 0.0)
     p = make_problem(**w)
     A = dev_tensor(p.A, p.dtype, device)
     B = dev_tensor(p.B, p.dtype, device)
@@ -95,8 +97,14 @@ def prepare(name: str, device, rotate: bool):
         copies = max(1, math.ceil(ROTATE_BYTES / max(1, s * (p.M * p.K + p.K * p.N))))
     As = [A] + [A.clone() for _ in range(copies - 1)]
     Bs = [B] + [B.clone() for _ in range(copies - 1)]
-    C = torch.empty((p.M, p.N), dtype=A.dtype, device=device)
-    return dict(p=p, As=As, Bs=Bs, C=C, epi=epi, slope=slope, copies=copies, alg_bytes=alg_bytes,
+    if beta != 0.0:
+        from gemm_inputs import make_c_old
+        C = dev_tensor(make_c_old(p.M, p.N, p.dtype, p.desc["seed"]), p.dtype, device)
+        alg_bytes += s * p.M * p.N   # the old C is read
+    else:
+        C = torch.empty((p.M, p.N), dtype=A.dtype, device=device)
+    return dict(p=p, As=As, Bs=Bs, C=C, epi=epi, slope=slope, alpha=alpha, beta=beta,
+                copies=copies, alg_bytes=alg_bytes,
                 flops=2.0 * p.M * p.N * p.K, dtype=DTYPE_NAMES[p.dtype])
 
 
@@ -118,7 +126,7 @@ def time_workload(name: str, steps: int, warmup: int, device, rotate: bool):
     def step(i):
         j = i % d["copies"]
         tg.gemm(d["As"][j], d["Bs"][j], trans_a=p.trans_a, trans_b=p.trans_b, epilogue=epi,
-                out=d["C"], workspace=ws, stream=stream.cuda_stream)
+                out=d["C"], alpha=d["alpha"], beta=d["beta"], workspace=ws, stream=stream.cuda_stream)
 
     for i in range(warmup):
         step(i)
@@ -148,6 +156,8 @@ def cpu_baseline(name: str, target_s: float):
     w = dict(WORKLOADS[name])
     epi = w.pop("epilogue", None)
     slope = w.pop("slope", 0.01)
+    alpha = w.pop("alpha", 1.0)
+    beta = w.pop("beta", 0.0)
     p = make_problem(**w)
     A64 = oracle.to_f64(p.A, p.dtype)
     B64 = oracle.to_f64(p.B, p.dtype)
@@ -427,6 +437,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "M": p.M, "N": p.N, "K": p.K,
                    "layout": ["NN", "TN", "NT", "TT"][p.trans], "epilogue": d["epi"] or "none",
+                   "alpha": d["alpha"], "beta": d["beta"],
                    "seed": p.desc["seed"], "dist": p.desc["dist"], "plan": {
                        k: r["plan"][k] for k in ("path_name", "tile_m", "tile_n", "split_k",
                                                   "tiles", "waves", "occupancy")}},

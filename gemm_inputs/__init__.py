@@ -155,6 +155,14 @@ def make_problem(M: int, N: int, K: int, dtype, trans: int = NN, dist: str = "un
                    dict(dist=dist, seed=seed, ld_pad=ld_pad))
 
 
+def make_c_old(M: int, N: int, dtype, seed: int) -> np.ndarray:
+    """Seeded old C for alpha/beta runs: i.i.d. U[-1, 1) from default_rng([seed, 7]),
+    rounded to the storage type (bfloat16 as uint16 bits), M x N row-major."""
+    d = dtype_code(dtype)
+    x = np.random.default_rng([seed, 7]).uniform(-1.0, 1.0, size=(M, N))
+    return round_to(x, d)
+
+
 def make_int_problem(M: int, N: int, K: int, dtype, trans: int, lo: int, hi: int,
                      seed: int = 0) -> Problem:
     """Integer-valued operands drawn uniformly from {lo..hi} (inclusive).
@@ -212,6 +220,9 @@ WORKLOADS = {
                             epilogue="leaky_relu", slope=0.01),
     "bf16_leaky_6912x2048x4096": dict(M=6912, N=2048, K=4096, dtype=BF16, trans=NN, dist="normal",
                                       seed=1, epilogue="leaky_relu", slope=0.01),
+    # the full BLAS statement C = alpha A.B + beta C_old (C_old from make_c_old, seed 1)
+    "f16_8192_alpha_beta": dict(M=8192, N=8192, K=8192, dtype=F16, trans=NN, dist="normal", seed=1,
+                                alpha=0.5, beta=1.0),
 }
 
 

@@ -4,7 +4,11 @@
  * Operation ("Matrix Multiplication Background User's Guide", sections 1-2,
  * in BLAS naming: A is M x K, B is K x N, C is M x N):
  *
- *     C[i][j] = epi( sum_{k < K} A(i,k) * B(k,j) )        (C is overwritten)
+ *     C[i][j] = epi( alpha * sum_{k < K} A(i,k) * B(k,j) + beta * C[i][j] )
+ *
+ * alpha = 1 and beta = 0 unless the epilogue sets TG_EPI_SCALE (the guide's
+ * full BLAS statement scales the product and adds a multiple of the old C);
+ * with beta = 0 the old C is not read (it may hold anything, NaN included).
  *
  * All matrices are row-major.  An operand may be stored transposed, as the
  * row-major array of its transpose (what the Triton matmul tutorial's
@@ -16,11 +20,12 @@
  *     C(i,j) = C[i*ldc + j]
  *
  * Inputs and output share one storage type (dtype); products are accumulated
- * in float32 and the epilogue is applied to the float32 sum before the single
- * rounding (nearest-even) to the output type.  The optional epilogue is a
- * leaky rectifier x >= 0 ? x : slope*x, the fused output transform the
- * Triton news article gives as the reason to hand-write matmul kernels
- * ("OpenAI open-sources Triton", matrix multiplication section).
+ * in float32, alpha * sum + beta * C (the old C widened to float32) is formed
+ * in float32, and epi is applied to it before the single rounding
+ * (nearest-even) to the output type.  epi is the identity or a leaky
+ * rectifier x >= 0 ? x : slope*x, the fused output transform the Triton news
+ * article gives as the reason to hand-write matmul kernels ("OpenAI
+ * open-sources Triton", matrix multiplication section).
  *
  * Leading dimensions (element counts):
  *     lda >= max(1, trans_a ? M : K),  ldb >= max(1, trans_b ? K : N),
@@ -35,7 +40,8 @@
  * waiting: results are valid once the stream has been synchronised.  C must
  * not overlap A or B.
  *
- * Quick returns: M == 0 or N == 0 does nothing; K == 0 writes epi(0) = 0.
+ * Quick returns: M == 0 or N == 0 does nothing; K == 0 or alpha == 0 writes
+ * epi(beta * C) without reading A or B (epi(0) = 0 when beta == 0).
  *
  * Errors: every entry point returns a tg_status; on failure nothing is
  * enqueued and tg_last_error() describes the cause (thread-local).
@@ -50,7 +56,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 100
+#define TG_VERSION 101
 
 /* storage type of A, B and C */
 enum tg_dtype { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 };
@@ -77,15 +83,23 @@ enum tg_status {
  * the tile, and splits K when M and N are small and K is large). */
 enum tg_path {
     TG_PATH_AUTO = -1,
-    TG_PATH_NONE = 0,   /* quick return (M == 0, N == 0) or K == 0 fill */
+    TG_PATH_NONE = 0,   /* quick return (M == 0, N == 0), or K == 0: C = epi(beta * C) */
     TG_PATH_MFMA = 1,   /* macro-tile matrix-core kernel (all storage types) */
     TG_PATH_SKINNY = 2, /* memory-bound narrow product (small N or small M), matrix cores */
     TG_PATH_GEMV = 3    /* M == 1 or N == 1: vector ALUs, no matrix cores */
 };
 
+/* flags of tg_epilogue */
+#define TG_EPI_SCALE 1u /* use alpha and beta (otherwise alpha = 1, beta = 0) */
+
+/* Output transform.  A zero-initialised struct (or NULL) is the plain product
+ * C = A.B; unknown kinds or flag bits are TG_ERR_ARG. */
 typedef struct tg_epilogue {
-    uint32_t kind; /* tg_epi_kind */
-    float slope;   /* negative-side slope of TG_EPI_LEAKY_RELU */
+    uint32_t kind;  /* tg_epi_kind */
+    float slope;    /* negative-side slope of TG_EPI_LEAKY_RELU */
+    uint32_t flags; /* TG_EPI_SCALE */
+    float alpha;    /* product scale, with TG_EPI_SCALE */
+    float beta;     /* scale of the old C, with TG_EPI_SCALE; 0 = C is not read */
 } tg_epilogue;
 
 /* Optional planner overrides (NULL = all automatic).  A forced tile reproduces

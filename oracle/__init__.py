@@ -11,6 +11,6 @@ random products have no printed counterpart on the source pages; for those the
 oracle's own fp64 result is the reference (no further pin exists).
 """
 from .oracle import (  # noqa: F401
-    EPI_NONE, EPI_LEAKY_RELU, gemm_full, gemm_points, to_f64, tolerance, check,
+    EPI_NONE, EPI_LEAKY_RELU, gemm_full, gemm_points, to_f64, scaled, tolerance, check,
     plant_fault, load, default_threads,
 )

@@ -10,6 +10,11 @@ float64 and C_ref the float64 value after the epilogue):
 
     |C - C_ref| <= 1e-4 * (|A||B|)_ij + 1e-6 + r_out * |C_ref|
 
+With alpha and beta (scaled()), (|A||B|)_ij becomes |alpha| (|A||B|)_ij +
+|beta C_old|: the float32 accumulation error scales with alpha, and forming
+alpha * sum + beta * C_old in float32 adds two roundings, far below 1e-4 of
+that sum of magnitudes.
+
 r_out is 0 for a float32 output, 1e-3 for float16 and 2^-8 for bfloat16.  The
 first two terms bound float32 accumulation in any order; the third is the
 rounding of the stored output.  1e-3 would be below bfloat16's own unit
@@ -138,6 +143,33 @@ def gemm_points(M, N, K, A, lda, trans_a, B, ldb, trans_b, I, J, dtype=F32, epi=
         raise ValueError(f"oracle_gemm_points rejected its arguments (rc={rc})")
     out, absout = out[:n], absout[:n]
     return (out, absout, int(macs[0])) if want_macs else (out, absout)
+
+
+def scaled(acc: np.ndarray, absab: np.ndarray, alpha: float, beta: float, c_old=None,
+           epi: int = EPI_NONE, slope: float = 0.0):
+    """The full BLAS statement C = epi(alpha * (A.B) + beta * C_old), in float64.
+
+    ``acc`` and ``absab`` are the plain product and (|A||B|) from gemm_full or
+    gemm_points (called with EPI_NONE); ``c_old`` is the old C widened to
+    float64, not used when ``beta`` is 0; with ``alpha`` 0 the product is not
+    used either (BLAS: A and B are not referenced).  Returns (C_ref, scale) where scale =
+    |alpha| (|A||B|)_ij + |beta C_old| replaces (|A||B|)_ij in tolerance().
+    """
+    acc = np.asarray(acc, dtype=np.float64)
+    if alpha == 0.0:
+        # BLAS: with alpha = 0, A and B are not referenced (a NaN there is no term)
+        x = np.zeros_like(acc)
+        scale = np.zeros_like(acc)
+    else:
+        x = alpha * acc
+        scale = abs(alpha) * np.asarray(absab, dtype=np.float64)
+    if beta != 0.0:
+        c = np.asarray(c_old, dtype=np.float64)
+        x = x + beta * c
+        scale = scale + abs(beta) * np.abs(c)
+    if epi == EPI_LEAKY_RELU:
+        x = np.where(x >= 0.0, x, slope * x)
+    return x, scale
 
 
 def tolerance(ref: np.ndarray, absab: np.ndarray, out_dtype: int) -> np.ndarray:

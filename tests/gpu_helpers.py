@@ -5,7 +5,7 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
-from gemm_inputs import BF16, F16, F32, Problem, sample_points
+from gemm_inputs import BF16, F16, F32, Problem, make_c_old, sample_points
 
 EPI_CODES = {None: 0, "none": 0, "leaky_relu": 1}
 
@@ -35,8 +35,12 @@ def from_device(t, d) -> np.ndarray:
     return c.numpy().astype(np.float64)
 
 
-def run_gpu(p: Problem, epilogue=None, slope=0.01, options=None, out_pad: int = 0, workspace=None):
-    """Run tg_gemm_ex on the problem; returns the float64 copy of C (M x N)."""
+def run_gpu(p: Problem, epilogue=None, slope=0.01, options=None, out_pad: int = 0, workspace=None,
+            alpha=1.0, beta=0.0, c_old=None):
+    """Run tg_gemm_ex on the problem; returns the float64 copy of C (M x N).
+
+    C starts as NaN (so an unwritten element, or an old C read with beta = 0,
+    shows), or as ``c_old`` (stored values) when given."""
     import torch
     import tiled_gemm_02_amd as tg
     A = to_device(p.A, p.dtype)
@@ -47,11 +51,13 @@ def run_gpu(p: Problem, epilogue=None, slope=0.01, options=None, out_pad: int = 
         C = Cw[:, :p.N]
     else:
         C = torch.full((p.M, p.N), float("nan"), dtype=torch_dtype(p.dtype), device="cuda:0")
+    if c_old is not None:
+        C.copy_(to_device(c_old, p.dtype))
     # the stored arrays may be padded: pass views of the logical width with the stored ld
     Av = A[:, : (p.M if p.trans_a else p.K)] if A.shape[1] else A
     Bv = B[:, : (p.K if p.trans_b else p.N)] if B.shape[1] else B
     tg.gemm(Av, Bv, trans_a=p.trans_a, trans_b=p.trans_b, epilogue=epi, out=C, options=options,
-            workspace=workspace)
+            workspace=workspace, alpha=alpha, beta=beta)
     torch.cuda.synchronize()
     got = from_device(C, p.dtype)
     if out_pad:
@@ -70,6 +76,19 @@ def check_full(p: Problem, epilogue=None, slope=0.01, options=None, out_pad=0, w
     got = run_gpu(p, epilogue, slope, options, out_pad, workspace)
     ref, absab = oracle_full(p, epilogue, slope)
     r = oracle.check(got, ref, absab, p.dtype)
+    return r, got, ref
+
+
+def check_scaled(p: Problem, alpha: float, beta: float, epilogue=None, slope=0.01, options=None,
+                 c_seed=0, workspace=None):
+    """C = epi(alpha A.B + beta C_old) against the oracle; C_old is a seeded draw."""
+    c_old = make_c_old(p.M, p.N, p.dtype, c_seed)
+    got = run_gpu(p, epilogue, slope, options, workspace=workspace, alpha=alpha, beta=beta,
+                  c_old=c_old)
+    acc, absab = oracle_full(p, None)
+    ref, scale = oracle.scaled(acc, absab, alpha, beta, oracle.to_f64(c_old, p.dtype),
+                               EPI_CODES[epilogue], slope)
+    r = oracle.check(got, ref, scale, p.dtype)
     return r, got, ref
 
 

@@ -33,7 +33,26 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert tg.tg_version() == 100
+    assert tg.tg_version() == 101
+
+
+def test_epilogue_struct_matches_header(tmp_path):
+    """The binding's tg_epilogue mirror has the header's field offsets and size
+    (checked with the host C compiler on the header itself)."""
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "tg_gemm.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(tg_epilogue), '
+                   'offsetof(tg_epilogue, kind), offsetof(tg_epilogue, slope), '
+                   'offsetof(tg_epilogue, flags), offsetof(tg_epilogue, alpha), '
+                   'offsetof(tg_epilogue, beta)); return 0; }\n')
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    E = tg.Epilogue
+    assert got == [ctypes.sizeof(E), E.kind.offset, E.slope.offset, E.flags.offset,
+                   E.alpha.offset, E.beta.offset]
 
 
 def test_argument_errors():
@@ -42,6 +61,7 @@ def test_argument_errors():
     assert tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, 7, 0) == tg.TG_ERR_ARG
     assert tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, F16, 9) == tg.TG_ERR_ARG
     assert tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, F16, 0, (5, 0.1)) == tg.TG_ERR_ARG
+    assert tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, F16, 0, tg.Epilogue(0, 0.0, 6, 1.0, 0.0)) == tg.TG_ERR_ARG
     # negative sizes and short leading dimensions
     assert tg.tg_gemm(-1, 4, 4, 1, 4, 1, 4, 1, 4, F16, 0) == tg.TG_ERR_ARG
     assert tg.tg_gemm(4, 4, 4, 1, 3, 1, 4, 1, 4, F16, 0) == tg.TG_ERR_ARG

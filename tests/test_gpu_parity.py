@@ -11,7 +11,7 @@ import pytest
 
 from gemm_inputs import (BF16, F16, F32, NN, NT, TN, TT, WORKLOADS, make_int_problem, make_problem,
                          layout, round_to)
-from tests.gpu_helpers import check_full, check_sampled, run_gpu, to_device
+from tests.gpu_helpers import check_full, check_sampled, check_scaled, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -319,3 +319,69 @@ def test_sweep_shapes_sampled(N):
     assert r["ok"], r
     r = check_sampled(p, n=1024, options=dict(tile_m=256, tile_n=128, split_k=1))
     assert r["ok"], r
+
+
+# ---------------------------------------------------------------- alpha and beta
+#
+# C = epi(alpha A.B + beta C_old) through every path that writes C: the macro
+# tiles (ping-pong, four-wave and register-staged kernels), split-K and its
+# reduction, the skinny stream, both GEMV forms, unaligned operands, K = 0 and
+# alpha = 0.  C_old is a seeded draw; with beta = 0 C starts as NaN and must
+# not be read.
+
+SCALED = [
+    # M, N, K, dtype, trans, ld_pad, options, alpha, beta, epilogue
+    (512, 512, 256, F16, NN, 0, dict(tile_m=256, tile_n=256, split_k=1), 0.5, -1.25, None),
+    (512, 512, 200, BF16, NT, 0, dict(tile_m=256, tile_n=256, split_k=1), 2.0, 0.5, "leaky_relu"),
+    (520, 296, 264, F16, TT, 0, dict(tile_m=128, tile_n=128, split_k=1), -1.0, 1.0, "leaky_relu"),
+    (304, 280, 520, BF16, TN, 0, dict(tile_m=256, tile_n=128, split_k=1), 1.5, 0.0, None),
+    (200, 136, 1000, F16, NN, 0, dict(split_k=3), 1.0, 1.0, None),
+    (200, 136, 1000, F32, NT, 0, dict(split_k=2), 0.75, -0.5, "leaky_relu"),
+    (130, 70, 90, F32, TT, 0, None, -1.0, 2.0, "leaky_relu"),
+    (100, 90, 70, F16, NN, 1, None, 2.0, 0.5, None),
+    (1000, 120, 1000, BF16, NN, 0, dict(path=2, split_k=1), 0.25, -0.5, "leaky_relu"),
+    (1000, 120, 1000, F16, NT, 0, dict(path=2, split_k=2), 1.5, 1.0, None),
+    (1, 1000, 777, F16, NN, 0, None, 2.0, 1.0, None),
+    (1, 520, 33, F32, NN, 0, None, -1.0, 0.5, "leaky_relu"),
+    (777, 1, 1031, BF16, NN, 0, None, -0.5, 1.0, "leaky_relu"),
+    (77, 1, 1031, F16, TN, 0, None, 3.0, -2.0, None),
+    (64, 64, 0, F16, NN, 0, None, 3.0, 0.5, "leaky_relu"),
+    (64, 48, 0, BF16, NN, 0, None, 1.0, 0.0, None),
+]
+
+
+@pytest.mark.parametrize("case", SCALED, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}")
+def test_alpha_beta(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, dtype, trans, ld_pad, opts, alpha, beta, epi = case
+    _say("case alpha/beta", case)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=31, ld_pad=ld_pad)
+    if opts and opts.get("path") == 2:
+        opts = dict(opts, path=tg.TG_PATH_SKINNY)
+    r, got, _ = check_scaled(p, alpha, beta, epilogue=epi, options=opts, c_seed=3)
+    assert r["ok"], (case, r)
+    assert np.isfinite(got).all()
+
+
+def test_alpha_zero_does_not_read_operands():
+    """BLAS: with alpha = 0, A and B are not referenced (NaN there is harmless)."""
+    p = make_problem(256, 192, 128, F16, NN, "uniform", seed=32)
+    p.A[...] = np.float16(np.nan)
+    p.B[...] = np.float16(np.nan)
+    r, got, _ = check_scaled(p, 0.0, -1.5, epilogue="leaky_relu", c_seed=4)
+    assert r["ok"], r
+    assert np.isfinite(got).all()
+
+
+def test_beta_needs_the_old_c():
+    import torch
+    import tiled_gemm_02_amd as tg
+    A = torch.zeros((8, 8), dtype=torch.float16, device="cuda:0")
+    with pytest.raises(ValueError):
+        tg.gemm(A, A, beta=1.0)
+    # unknown flag bits are an argument error
+    C = torch.zeros((8, 8), dtype=torch.float16, device="cuda:0")
+    bad = tg.Epilogue(0, 0.0, 2, 1.0, 0.0)
+    with pytest.raises(tg.TgError):
+        tg.gemm(A, A, out=C, epilogue=bad)
+

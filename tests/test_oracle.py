@@ -229,6 +229,70 @@ def test_integer_products_exact():
     np.testing.assert_array_equal(Z, ref.astype(float))
 
 
+# ---------------------------------------------------------------- alpha and beta
+
+def _brute(Alog, Blog):
+    """Exact integer product by Python loops (independent of the oracle's C loop)."""
+    M, K = Alog.shape
+    N = Blog.shape[1]
+    return np.array([[sum(int(Alog[i, k]) * int(Blog[k, j]) for k in range(K)) for j in range(N)]
+                     for i in range(M)], dtype=float)
+
+
+def test_scaled_beta_cancels_the_product():
+    """C_old = A.B (by brute force) and beta = -1: alpha = 1 gives exactly 0,
+    alpha = 3 gives exactly 2 A.B -- a dropped term, a wrong sign or the wrong
+    operand scaled all break one of them."""
+    rng = np.random.default_rng(21)
+    A = rng.integers(-3, 4, (5, 7)).astype(float)
+    B = rng.integers(-3, 4, (7, 6)).astype(float)
+    P = _brute(A, B)
+    acc, absab = full(A, B)
+    Z, _ = oracle.scaled(acc, absab, 1.0, -1.0, P)
+    np.testing.assert_array_equal(Z, np.zeros_like(P))
+    Z, _ = oracle.scaled(acc, absab, 3.0, -1.0, P)
+    np.testing.assert_array_equal(Z, 2.0 * P)
+
+
+def test_scaled_alpha_zero_and_homogeneity():
+    rng = np.random.default_rng(22)
+    A = rng.integers(-3, 4, (4, 9)).astype(float)
+    B = rng.integers(-3, 4, (9, 5)).astype(float)
+    Cold = rng.integers(-5, 6, (4, 5)).astype(float)
+    acc, absab = full(A, B)
+    # alpha = 0: only the old C remains, scaled; the product is not referenced
+    Z, _ = oracle.scaled(acc, absab, 0.0, 0.5, Cold)
+    np.testing.assert_array_equal(Z, Cold / 2)
+    Z, _ = oracle.scaled(np.full_like(acc, np.nan), absab, 0.0, 0.5, Cold)
+    np.testing.assert_array_equal(Z, Cold / 2)
+    # beta = 0: the product scales linearly and the old C is not used (NaN is harmless)
+    Z1, _ = oracle.scaled(acc, absab, 1.0, 0.0, np.full_like(Cold, np.nan))
+    Z4, _ = oracle.scaled(acc, absab, -4.0, 0.0, np.full_like(Cold, np.nan))
+    np.testing.assert_array_equal(Z1, _brute(A, B))
+    np.testing.assert_array_equal(Z4, -4.0 * Z1)
+
+
+def test_scaled_epilogue_acts_after_the_sum():
+    """With A = I: alpha B + beta C_old goes negative where alpha B alone does
+    not, and the rectifier must see the sum."""
+    B = np.array([[1.0, 2.0, -1.0]])
+    Cold = np.array([[-3.0, -1.0, 4.0]])
+    acc, absab = full(np.eye(1), B)
+    Z, _ = oracle.scaled(acc, absab, 1.0, 1.0, Cold, oracle.EPI_LEAKY_RELU, 0.5)
+    np.testing.assert_array_equal(Z, np.array([[-1.0, 1.0, 3.0]]))
+
+
+def test_scaled_tolerance_scale_by_brute_force():
+    rng = np.random.default_rng(23)
+    A = rng.integers(-3, 4, (3, 8)).astype(float)
+    B = rng.integers(-3, 4, (8, 4)).astype(float)
+    Cold = rng.integers(-5, 6, (3, 4)).astype(float)
+    acc, absab = full(A, B)
+    _, scale = oracle.scaled(acc, absab, -2.0, 0.25, Cold)
+    expect = 2.0 * _brute(np.abs(A), np.abs(B)) + 0.25 * np.abs(Cold)
+    np.testing.assert_array_equal(scale, expect)
+
+
 # ---------------------------------------------------------------- tolerance
 
 def test_tolerance_admits_correctly_rounded_outputs():

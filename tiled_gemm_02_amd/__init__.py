@@ -32,8 +32,12 @@ class TgError(RuntimeError):
         self.code = code
 
 
+TG_EPI_SCALE = 1   # tg_epilogue.flags: use alpha and beta
+
+
 class Epilogue(ctypes.Structure):
-    _fields_ = [("kind", ctypes.c_uint32), ("slope", ctypes.c_float)]
+    _fields_ = [("kind", ctypes.c_uint32), ("slope", ctypes.c_float), ("flags", ctypes.c_uint32),
+                ("alpha", ctypes.c_float), ("beta", ctypes.c_float)]
 
 
 class Options(ctypes.Structure):
@@ -97,12 +101,16 @@ def _check(rc: int) -> int:
     return rc
 
 
-def _epi(epilogue) -> ctypes.POINTER(Epilogue) | None:
-    if epilogue is None:
-        return None
+def _epi(epilogue, alpha=1.0, beta=0.0) -> ctypes.POINTER(Epilogue) | None:
+    """tg_epilogue for (kind or (kind, slope) or "leaky_relu"/"none" or None, alpha, beta)."""
+    scaled = alpha != 1.0 or beta != 0.0
     if isinstance(epilogue, Epilogue):
         return ctypes.pointer(epilogue)
-    if isinstance(epilogue, tuple):
+    if epilogue is None and not scaled:
+        return None
+    if epilogue is None:
+        kind, slope = TG_EPI_NONE, 0.0
+    elif isinstance(epilogue, tuple):
         kind, slope = epilogue
     elif epilogue in ("leaky_relu", TG_EPI_LEAKY_RELU):
         kind, slope = TG_EPI_LEAKY_RELU, 0.01
@@ -112,7 +120,8 @@ def _epi(epilogue) -> ctypes.POINTER(Epilogue) | None:
         raise ValueError(f"unknown epilogue {epilogue!r}")
     if kind == "leaky_relu":
         kind = TG_EPI_LEAKY_RELU
-    return ctypes.pointer(Epilogue(int(kind), float(slope)))
+    return ctypes.pointer(Epilogue(int(kind), float(slope), TG_EPI_SCALE if scaled else 0,
+                                   float(alpha), float(beta)))
 
 
 def _opts(options) -> ctypes.POINTER(Options) | None:
@@ -184,18 +193,21 @@ def _ld(t) -> int:
     if t.dim() != 2:
         raise ValueError("operands must be 2-D")
     rows, cols = t.shape
+    if t.numel() == 0:
+        return max(cols, 1)   # no element is addressed; any ld >= the width is valid
     if cols > 1 and t.stride(1) != 1:
         raise ValueError("operands must be row-major (last stride 1); pass a transpose flag instead")
     return max(int(t.stride(0)) if rows > 1 else cols, cols, 1)
 
 
 def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, out=None,
-         options=None, workspace=None, stream=None):
-    """C = epilogue(op(A) . op(B)) on the tensors' device.
+         alpha: float = 1.0, beta: float = 0.0, options=None, workspace=None, stream=None):
+    """C = epilogue(alpha * op(A) . op(B) + beta * C) on the tensors' device.
 
     A is the stored array: M x K, or K x M when ``trans_a``; B is K x N, or
     N x K when ``trans_b``.  Returns C (M x N, row-major, A's dtype); ``out``
-    may be a preallocated (possibly strided) M x N tensor.
+    may be a preallocated (possibly strided) M x N tensor, and holds the old C
+    when ``beta`` is not 0 (it is not read when ``beta`` is 0).
     """
     import torch
     if A.dtype != B.dtype:
@@ -206,6 +218,8 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, o
     if Kb != K:
         raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
     if out is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs out= (the old C)")
         out = torch.empty((M, N), dtype=A.dtype, device=A.device)
     elif out.shape != (M, N) or out.dtype != A.dtype:
         raise ValueError("out has the wrong shape or dtype")
@@ -217,9 +231,10 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, o
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if M == 0 or N == 0:
         return out
-    rc = tg_gemm_ex(M, N, K, A.data_ptr() if A.numel() else None, _ld(A),
-                    B.data_ptr() if B.numel() else None, _ld(B), out.data_ptr(), _ld(out), dtype,
-                    trans, epilogue, options, ws_ptr, ws_bytes, stream)
+    epi = _epi(epilogue, alpha, beta)
+    rc = load().tg_gemm_ex(M, N, K, A.data_ptr() if A.numel() else None, _ld(A),
+                           B.data_ptr() if B.numel() else None, _ld(B), out.data_ptr(), _ld(out),
+                           dtype, trans, epi, _opts(options), ws_ptr, ws_bytes, stream)
     _check(rc)
     return out
 

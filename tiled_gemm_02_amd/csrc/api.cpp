@@ -81,22 +81,23 @@ int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec)
 }
 
 hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, int N, void *C,
-                                int64_t ldc, int epi, float slope, int c_vec, hipStream_t s)
+                                int64_t ldc, const OutEpi &oe, int c_vec, hipStream_t s)
 {
     switch (dtype) {
-    case TG_F16: return launch_splitk_reduce_f16(ws, splits, M, N, C, ldc, epi, slope, c_vec, s);
-    case TG_BF16: return launch_splitk_reduce_bf16(ws, splits, M, N, C, ldc, epi, slope, c_vec, s);
-    case TG_F32: return launch_splitk_reduce_f32(ws, splits, M, N, C, ldc, epi, slope, c_vec, s);
+    case TG_F16: return launch_splitk_reduce_f16(ws, splits, M, N, C, ldc, oe, c_vec, s);
+    case TG_BF16: return launch_splitk_reduce_bf16(ws, splits, M, N, C, ldc, oe, c_vec, s);
+    case TG_F32: return launch_splitk_reduce_f32(ws, splits, M, N, C, ldc, oe, c_vec, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fill_zero(int dtype, void *C, int M, int N, int64_t ldc, hipStream_t s)
+hipError_t launch_scale_c(int dtype, void *C, int M, int N, int64_t ldc, const OutEpi &oe,
+                          hipStream_t s)
 {
     switch (dtype) {
-    case TG_F16: return launch_fill_zero_f16(C, M, N, ldc, s);
-    case TG_BF16: return launch_fill_zero_bf16(C, M, N, ldc, s);
-    case TG_F32: return launch_fill_zero_f32(C, M, N, ldc, s);
+    case TG_F16: return launch_scale_c_f16(C, M, N, ldc, oe, s);
+    case TG_BF16: return launch_scale_c_bf16(C, M, N, ldc, oe, s);
+    case TG_F32: return launch_scale_c_f32(C, M, N, ldc, oe, s);
     }
     return hipErrorInvalidValue;
 }
@@ -223,6 +224,8 @@ static int check_args(int64_t M, int64_t N, int64_t K, const void *A, int64_t ld
         return fail(TG_ERR_ARG, "unknown trans %d", trans);
     if (epi && epi->kind != TG_EPI_NONE && epi->kind != TG_EPI_LEAKY_RELU)
         return fail(TG_ERR_ARG, "unknown epilogue kind %u", epi->kind);
+    if (epi && (epi->flags & ~TG_EPI_SCALE) != 0)
+        return fail(TG_ERR_ARG, "unknown epilogue flags 0x%x", epi->flags);
     if (M < 0 || N < 0 || K < 0)
         return fail(TG_ERR_ARG, "negative dimension (M=%lld N=%lld K=%lld)", (long long)M,
                     (long long)N, (long long)K);
@@ -276,16 +279,29 @@ static Chip device_chip(const DeviceInfo &d)
 
 // ---------------------------------------------------------------- execution
 
+// The public epilogue as the kernels' output transform (NULL or a zeroed
+// struct: the plain product).
+static OutEpi out_epi(const tg_epilogue *epi)
+{
+    OutEpi oe;
+    oe.kind = epi ? (int)epi->kind : TG_EPI_NONE;
+    oe.slope = epi ? epi->slope : 0.0f;
+    const bool scaled = epi && (epi->flags & TG_EPI_SCALE);
+    oe.alpha = scaled ? epi->alpha : 1.0f;
+    oe.beta = scaled ? epi->beta : 0.0f;
+    return oe;
+}
+
 static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const void *B, void *C,
                     const tg_epilogue *epi, void *ws, hipStream_t s)
 {
-    const int epi_kind = epi ? (int)epi->kind : TG_EPI_NONE;
-    const float slope = epi ? epi->slope : 0.0f;
+    const OutEpi oe = out_epi(epi);
     const int E = chunk_elems(p.dtype);
     hipError_t e = hipSuccess;
-    if (pl.path == TG_PATH_NONE) {
+    if (pl.path == TG_PATH_NONE || oe.alpha == 0.0f) {
+        // K == 0 or alpha == 0: no product term; A and B are not read
         if (p.M > 0 && p.N > 0)
-            e = launch_fill_zero(p.dtype, C, (int)p.M, (int)p.N, p.ldc, s);
+            e = launch_scale_c(p.dtype, C, (int)p.M, (int)p.N, p.ldc, oe, s);
     } else if (pl.path == TG_PATH_MFMA) {
         MfmaArgs a{};
         a.A = A;
@@ -305,8 +321,7 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.splits = pl.split_k;
         a.tiles_m = (int)((p.M + pl.tile_m - 1) / pl.tile_m);
         a.tiles_n = (int)((p.N + pl.tile_n - 1) / pl.tile_n);
-        a.epi = epi_kind;
-        a.slope = slope;
+        a.oe = oe;
         const int cb = elem_bytes(p.dtype);
         a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
         if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, p.M, p.N, p.K, p.lda, p.ldb))
@@ -315,7 +330,7 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
             e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);
         if (e == hipSuccess && pl.split_k > 1)
             e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, (int)p.M, (int)p.N, C,
-                                     p.ldc, epi_kind, slope, a.c_vec, s);
+                                     p.ldc, oe, a.c_vec, s);
     } else if (pl.path == TG_PATH_SKINNY) {
         SkinnyArgs a{};
         a.A = A;
@@ -335,22 +350,20 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.splits = pl.split_k;
         a.nrb = (int)((p.M + kSkRows - 1) / kSkRows);
         a.skew = kSkinnySkew;
-        a.epi = epi_kind;
-        a.slope = slope;
+        a.oe = oe;
         const int cb = elem_bytes(p.dtype);
         a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
         e = launch_skinny(p.dtype, (p.trans & TG_TRANS_B) != 0, a, s);
         if (e == hipSuccess && pl.split_k > 1)
             e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, (int)p.M, (int)p.N, C,
-                                     p.ldc, epi_kind, slope, a.c_vec, s);
+                                     p.ldc, oe, a.c_vec, s);
     } else if (pl.path == TG_PATH_GEMV) {
         const bool ta = p.trans & TG_TRANS_A, tb = p.trans & TG_TRANS_B;
         const bool rows_form = pl.tile_m == 4;
         GemvArgs g{};
         g.ws = (float *)ws;
         g.K = (int)p.K;
-        g.epi = epi_kind;
-        g.slope = slope;
+        g.oe = oe;
         g.ksplit = pl.split_k;
         g.O = C;
         if (p.M == 1) {

@@ -1,18 +1,18 @@
-// aux_kernels.hpp -- split-K reduction and the K == 0 fill.
+// aux_kernels.hpp -- split-K reduction and the K == 0 / alpha == 0 output pass.
 #pragma once
 
 #include "common.hpp"
 
 namespace tg {
 
-// C[m][n] = epi( sum_{z < splits} ws[z][m][n] ), summed in increasing z so the
+// C[m][n] = out(sum_{z < splits} ws[z][m][n]), summed in increasing z so the
 // result does not depend on which split finished first.  Splitting K needs
 // this final reduction ("Matrix Multiplication Background User's Guide",
 // section 2.3).  One thread per 4 consecutive outputs of a row.
 template <typename Tr>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ ws, int splits,
                                                             int M, int N, void *C_, int64_t ldc,
-                                                            int epi, float slope, int c_vec)
+                                                            OutEpi oe, int c_vec)
 {
     using T = typename Tr::T;
     T *C = (T *)C_;
@@ -53,32 +53,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
                         s[e] += v[u][e];
                 }
         }
-        T *dst = C + (int64_t)m * ldc + n;
-        T v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            v[e] = Tr::from_f32(apply_epi(s[e], epi, slope));
-        if (c_vec && n + 3 < N) {
-            if constexpr (Tr::kBytes == 2) {
-                u32x2 w;
-                w[0] = __builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
-                w[1] = __builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
-                *(u32x2 *)dst = w;
-            } else {
-                *(f32x4 *)dst = f32x4{v[0], v[1], v[2], v[3]};
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (n + e < N)
-                    dst[e] = v[e];
-        }
+        store_out4<Tr>(C + (int64_t)m * ldc + n, f32x4{s[0], s[1], s[2], s[3]}, N - n, c_vec && n + 3 < N, oe);
     }
 }
 
-// K == 0: the empty sum is 0 and both epilogues map 0 to 0.
+// K == 0 or alpha == 0: the product term is 0, so C = epi(beta * C) (A and B
+// are not read; with beta == 0 this writes epi(0) = 0 and does not read C).
 template <typename Tr>
-__global__ __launch_bounds__(256) void fill_zero_kernel(void *C_, int M, int N, int64_t ldc)
+__global__ __launch_bounds__(256) void scale_c_kernel(void *C_, int M, int N, int64_t ldc, OutEpi oe)
 {
     using T = typename Tr::T;
     T *C = (T *)C_;
@@ -87,7 +69,9 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(void *C_, int M, int N, 
          idx += (int64_t)gridDim.x * 256) {
         const int m = (int)(idx / N);
         const int n = (int)(idx - (int64_t)m * N);
-        C[(int64_t)m * ldc + n] = Tr::from_f32(0.0f);
+        T *c = C + (int64_t)m * ldc + n;
+        const float c_old = oe.beta != 0.0f ? Tr::to_f32(*c) : 0.0f;
+        *c = Tr::from_f32(apply_epi(oe.beta != 0.0f ? oe.beta * c_old : 0.0f, oe.kind, oe.slope));
     }
 }
 

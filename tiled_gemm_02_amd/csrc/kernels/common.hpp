@@ -23,8 +23,28 @@ enum : int { kEpiNone = 0, kEpiLeaky = 1 };
 
 __device__ __forceinline__ float apply_epi(float x, int epi, float slope)
 {
-    // leaky rectifier on the float32 accumulator, before output rounding
+    // leaky rectifier on the float32 value, before output rounding
     return (epi == kEpiLeaky && x < 0.0f) ? x * slope : x;
+}
+
+// The output transform every kernel applies when it writes C:
+//     C = epi(alpha * acc + beta * C_old),
+// formed in float32 before the single rounding; C_old is read only when
+// beta != 0 (with beta == 0 it may hold anything).  alpha = 1, beta = 0 leave
+// acc unchanged bit for bit.
+struct OutEpi {
+    int kind;      // kEpiNone / kEpiLeaky
+    float slope;
+    float alpha;
+    float beta;
+};
+
+__device__ __forceinline__ float out_value(const OutEpi &oe, float acc, float c_old)
+{
+    float x = oe.alpha * acc;
+    if (oe.beta != 0.0f)
+        x += oe.beta * c_old;
+    return apply_epi(x, oe.kind, oe.slope);
 }
 
 // Bit reinterpretation of one 32-bit lane value.  The argument is taken by
@@ -137,6 +157,59 @@ __device__ __forceinline__ void transpose_block(const u32x4 *in, u32x4 *out)
                 o[p] = __builtin_amdgcn_perm(in[2 * p + 1][w], in[2 * p][w], sel);
             out[j] = o;
         }
+    }
+}
+
+// Writes out_value(acc[e], C_old[e]) to dst[0 .. 3] of one row of C, skipping
+// elements at or past `avail` (columns left in the row).  vec: the four
+// elements are one aligned group (8 bytes of 16-bit values, 16 of float32)
+// wholly inside the row; then C_old is read and C written with one access each.
+template <typename Tr>
+__device__ __forceinline__ void store_out4(typename Tr::T *dst, const f32x4 &acc, int avail, bool vec,
+                                           const OutEpi &oe)
+{
+    using T = typename Tr::T;
+    float c_old[4] = {0.f, 0.f, 0.f, 0.f};
+    if (oe.beta != 0.0f) {
+        if (vec) {
+            if constexpr (Tr::kBytes == 2) {
+                const u32x2 w = *(const u32x2 *)dst;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t word = w[e >> 1];
+                    c_old[e] = Tr::to_f32(__builtin_bit_cast(T, (uint16_t)(word >> (16 * (e & 1)))));
+                }
+            } else {
+                const f32x4 v = *(const f32x4 *)dst;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    c_old[e] = v[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (e < avail)
+                    c_old[e] = Tr::to_f32(dst[e]);
+        }
+    }
+    T o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = Tr::from_f32(out_value(oe, acc[e], c_old[e]));
+    if (vec) {
+        if constexpr (Tr::kBytes == 2) {
+            u32x2 w;
+            w[0] = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
+            w[1] = (uint32_t)__builtin_bit_cast(uint16_t, o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
+            *(u32x2 *)dst = w;
+        } else {
+            *(f32x4 *)dst = f32x4{o[0], o[1], o[2], o[3]};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < avail)
+                dst[e] = o[e];
     }
 }
 

@@ -29,9 +29,18 @@ struct GemvArgs {
     int K;
     int ksplit;
     int rows_per_split;
-    int epi;
-    float slope;
+    OutEpi oe;       // output transform
 };
+
+// out(j) = epi(alpha * acc + beta * out_old(j))
+template <typename Tr>
+__device__ __forceinline__ void gemv_store(const GemvArgs &p, int64_t j, float acc)
+{
+    using T = typename Tr::T;
+    T *o = (T *)p.O + j * p.os;
+    const float c_old = p.oe.beta != 0.0f ? Tr::to_f32(*o) : 0.0f;
+    *o = Tr::from_f32(out_value(p.oe, acc, c_old));
+}
 
 template <typename Tr>
 __device__ __forceinline__ float load_scalar(const void *p, int64_t i)
@@ -145,10 +154,9 @@ __global__ __launch_bounds__(256) void gemv_cols_kernel(GemvArgs p)
         for (int e = 0; e < E; ++e)
             W[e] = s[e];
     } else {
-        T *O = (T *)p.O;
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            O[(int64_t)(col + e) * p.os] = Tr::from_f32(apply_epi(s[e], p.epi, p.slope));
+            gemv_store<Tr>(p, col + e, s[e]);
     }
 }
 
@@ -201,11 +209,10 @@ __global__ __launch_bounds__(256) void gemv_cols_generic_kernel(GemvArgs p)
             if (col + e < p.n)
                 W[col + e] = s[e];
     } else {
-        T *O = (T *)p.O;
 #pragma unroll
         for (int e = 0; e < E; ++e)
             if (col + e < p.n)
-                O[(int64_t)(col + e) * p.os] = Tr::from_f32(apply_epi(s[e], p.epi, p.slope));
+                gemv_store<Tr>(p, col + e, s[e]);
     }
 }
 
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(GemvArgs p)
             if (z0 + u < p.ksplit)
                 s += v[u];
     }
-    ((T *)p.O)[(int64_t)j * p.os] = Tr::from_f32(apply_epi(s, p.epi, p.slope));
+    gemv_store<Tr>(p, j, s);
 }
 
 // rows form.  One wave per output: lanes stride over 16-byte chunks of the
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(GemvArgs p)
     for (int off = 32; off >= 1; off >>= 1)
         acc += __shfl_xor(acc, off, 64);
     if (lane == 0)
-        ((T *)p.O)[(int64_t)i * p.os] = Tr::from_f32(apply_epi(acc, p.epi, p.slope));
+        gemv_store<Tr>(p, i, acc);
 }
 
 }  // namespace tg

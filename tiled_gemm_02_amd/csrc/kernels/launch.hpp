@@ -20,8 +20,10 @@ int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec);
 hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s);
 int mfma2_occupancy(int dtype, int trans, int bm, int bn);
 hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, int N, void *C,
-                                int64_t ldc, int epi, float slope, int c_vec, hipStream_t s);
-hipError_t launch_fill_zero(int dtype, void *C, int M, int N, int64_t ldc, hipStream_t s);
+                                int64_t ldc, const OutEpi &oe, int c_vec, hipStream_t s);
+// C = epi(beta * C): K == 0 or alpha == 0.
+hipError_t launch_scale_c(int dtype, void *C, int M, int N, int64_t ldc, const OutEpi &oe,
+                          hipStream_t s);
 // rows_form: outputs are contiguous dot products; else column streaming.
 // lpr: lanes per row segment of the vector cols kernel (columns per workgroup = lpr x
 // elements per 16 bytes).
@@ -34,9 +36,9 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
                                   hipStream_t s);                                                \
     int mfma_occupancy_##NAME(int trans, int bm, int bn, bool vec);                              \
     hipError_t launch_splitk_reduce_##NAME(const float *ws, int splits, int M, int N, void *C,   \
-                                           int64_t ldc, int epi, float slope, int c_vec,         \
-                                           hipStream_t s);                                       \
-    hipError_t launch_fill_zero_##NAME(void *C, int M, int N, int64_t ldc, hipStream_t s);       \
+                                           int64_t ldc, OutEpi oe, int c_vec, hipStream_t s);    \
+    hipError_t launch_scale_c_##NAME(void *C, int M, int N, int64_t ldc, OutEpi oe,             \
+                                     hipStream_t s);                                             \
     hipError_t launch_gemv_##NAME(bool rows_form, bool vec, int lpr, const GemvArgs &a,          \
                                   hipStream_t s);                                                \
     hipError_t launch_skinny_##NAME(bool trans_b, const SkinnyArgs &a, hipStream_t s);           \

@@ -47,8 +47,7 @@ struct MfmaArgs {
     int kps;          // K range per split (multiple of BK)
     int splits;
     int tiles_m, tiles_n;
-    int epi;
-    float slope;
+    OutEpi oe;        // output transform
     int c_vec;        // 1: C rows are 16-byte aligned and ldc % 4 == 0
 };
 
@@ -307,26 +306,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs p)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int n = n0 + wn * WN + j * 16 + 4 * fg;
-            T *dst = C + (int64_t)m * p.ldc + n;
-            T v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = Tr::from_f32(apply_epi(acc[i][j][e], p.epi, p.slope));
-            if (p.c_vec && n + 3 < p.N) {
-                if constexpr (Tr::kBytes == 2) {
-                    u32x2 w;
-                    w[0] = __builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
-                    w[1] = __builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
-                    *(u32x2 *)dst = w;
-                } else {
-                    *(f32x4 *)dst = f32x4{v[0], v[1], v[2], v[3]};
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < p.N)
-                        dst[e] = v[e];
-            }
+            if (n >= p.N)
+                continue;
+            store_out4<Tr>(C + (int64_t)m * p.ldc + n, acc[i][j], p.N - n, p.c_vec && n + 3 < p.N, p.oe);
         }
     }
 }

@@ -310,22 +310,7 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
             }
             return;
         }
-        T *dst = C + (int64_t)m * p.ldc + n;
-        T o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            o[e] = Tr::from_f32(apply_epi(v[e], p.epi, p.slope));
-        if (p.c_vec && n + 3 < p.N) {
-            u32x2 w;
-            w[0] = __builtin_bit_cast(uint16_t, o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
-            w[1] = __builtin_bit_cast(uint16_t, o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
-            *(u32x2 *)dst = w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (n + e < p.N)
-                    dst[e] = o[e];
-        }
+        store_out4<Tr>(C + (int64_t)m * p.ldc + n, v, p.N - n, p.c_vec && n + 3 < p.N, p.oe);
     };
 #pragma unroll
     for (int i = 0; i < FM; ++i)

@@ -51,8 +51,7 @@ struct SkinnyArgs {
     int splits;
     int nrb;         // row blocks, ceil(M / kSkRows)
     int skew;        // stages between the start points of consecutive XCDs
-    int epi;
-    float slope;
+    OutEpi oe;       // output transform
     int c_vec;
 };
 
@@ -302,24 +301,7 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
                         dst[e] = s[e];
                 continue;
             }
-            T v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v[e] = Tr::from_f32(apply_epi(s[e], p.epi, p.slope));
-            T *dst = (T *)p.C + (int64_t)m * p.ldc + ncol;
-            if (p.c_vec && ncol + 3 < p.N) {
-                u32x2 w;
-                w[0] = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
-                w[1] = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) |
-                       ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
-                *(u32x2 *)dst = w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (ncol + e < p.N)
-                        dst[e] = v[e];
-            }
+            store_out4<Tr>((T *)p.C + (int64_t)m * p.ldc + ncol, s, p.N - ncol, p.c_vec && ncol + 3 < p.N, p.oe);
         }
     }
 #else
