@@ -294,7 +294,7 @@ def traffic_summarize(root: str):
 
 # ---------------------------------------------------------------- quantization sweep
 
-def sweep(out_path: str, step: int, reps: int = 5):
+def sweep(out_path: str, step: int, reps: int = 5, tune: bool = False):
     """fp16 M=2304, K=4096, N = 1536 .. 6144: the planner's tile against a fixed 256 x 256 one.
 
     Inputs are N(0,1)/sqrt(K), seeded; each point is the median of `reps` timed calls after two
@@ -328,6 +328,7 @@ def sweep(out_path: str, step: int, reps: int = 5):
         return sorted(ts)[len(ts) // 2]
 
     rows = []
+    tuned = []   # (N, planner TFLOP/s, best TFLOP/s, best options)
     for N in sweep_ns(step=step):
         B = Bfull[:, :N].contiguous()
         C = Cfull[:, :N]
@@ -337,8 +338,14 @@ def sweep(out_path: str, step: int, reps: int = 5):
         fl = 2.0 * M * N * K
         rows.append((N, pl["tile_m"], pl["tile_n"], pl["split_k"], pl["tiles"], pl["waves"],
                      fl / ms / 1e9, fl / ms_f / 1e9, pl["pred_eff"]))
-        log(f"N={N} plan {pl['tile_m']}x{pl['tile_n']} tiles {pl['tiles']} waves {pl['waves']}: "
-            f"{rows[-1][6]:.0f} TFLOP/s (fixed 256x256: {rows[-1][7]:.0f})")
+        msg = (f"N={N} plan {pl['tile_m']}x{pl['tile_n']} tiles {pl['tiles']} waves {pl['waves']}: "
+               f"{rows[-1][6]:.0f} TFLOP/s (fixed 256x256: {rows[-1][7]:.0f})")
+        if tune:
+            best, _ = tg.autotune(A, B, out=C, workspace=ws, reps=3)
+            ms_b = timed(B, C, None if best["path"] == tg.TG_PATH_AUTO else best)
+            tuned.append((N, fl / ms / 1e9, fl / ms_b / 1e9, best))
+            msg += f" (autotuned {best['tile_m']}x{best['tile_n']} s{best['split_k']}: {fl / ms_b / 1e9:.0f})"
+        log(msg)
     better = sum(1 for r in rows if r[6] >= r[7] * 0.98)
     mean_p = sum(r[6] for r in rows) / len(rows)
     mean_f = sum(r[7] for r in rows) / len(rows)
@@ -364,6 +371,64 @@ def sweep(out_path: str, step: int, reps: int = 5):
                      f"{band[0][4]}-{band[-1][4]} | {band[0][5]} | {mmm(6)} | {mmm(7)} |")
         i = j + 1
     lines.append("")
+    if tuned:
+        ratio = sorted(t[1] / t[2] for t in tuned)
+        within = sum(1 for r in ratio if r >= 0.95)
+        lines += ["## The planner against benchmark mode", "",
+                  f"At each point `tg_autotune` timed every candidate (planner's choice, every tile "
+                  f"x split 1-8, skinny); the winner and the planner were then timed again the "
+                  f"same way.  Planner / best TFLOP/s: median {ratio[len(ratio) // 2]:.3f}, "
+                  f"minimum {ratio[0]:.3f}; within 5 % at {within} of {len(tuned)} points.", "",
+                  "| N | Planner TFLOP/s | Best TFLOP/s | Best plan |", "|---|---|---|---|"]
+        for (N, tp, tb, b) in tuned:
+            if tp / tb < 0.95:
+                plan = "planner's" if b["path"] == tg.TG_PATH_AUTO else (
+                    f"{b['tile_m']}x{b['tile_n']} split {b['split_k']}" if b["path"] == tg.TG_PATH_MFMA
+                    else f"skinny split {b['split_k']}")
+                lines.append(f"| {N} | {tp:.0f} | {tb:.0f} | {plan} |")
+        lines += ["", "(rows listed: points where the planner is more than 5 % below the best)", ""]
+    open(out_path, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def align_sweep(out_path: str, reps: int = 5):
+    """fp16 NN M = N = 4096, K = 4096 + d for d = 0 .. 16: 16-byte-aligned rows (d % 8 == 0)
+    take the LDS-DMA kernels, the others the element-wise load path (the K-alignment
+    effect of "Matrix Multiplication Background User's Guide", section 3.1)."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    from gemm_inputs import F16, NN
+    device = torch.device("cuda:0")
+    M = N = 4096
+    stream = torch.cuda.current_stream(device)
+    g = torch.Generator(device=device).manual_seed(6)
+    lines = ["# K-alignment sweep: fp16 NN, M = N = 4096, K = 4096 + d", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"python3 bench.py --align-sweep {out_path}", "```", "",
+             "| K | K mod 8 | Path | Tile | Split | Vector loads | TFLOP/s |", "|---|---|---|---|---|---|---|"]
+    for d in range(17):
+        K = 4096 + d
+        A = (torch.randn((M, K), generator=g, device=device) / math.sqrt(K)).half()
+        B = (torch.randn((K, N), generator=g, device=device) / math.sqrt(K)).half()
+        C = torch.empty((M, N), dtype=torch.float16, device=device)
+        pl = tg.plan_for(A, B)
+        for _ in range(2):
+            tg.gemm(A, B, out=C, stream=stream.cuda_stream)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            tg.gemm(A, B, out=C, stream=stream.cuda_stream)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        tf = 2.0 * M * N * K / ms / 1e9
+        # plan_for assumes packed operands; the real call sees the same strides here
+        lines.append(f"| {K} | {K % 8} | {pl['path_name']} | {pl['tile_m']}x{pl['tile_n']} | "
+                     f"{pl['split_k']} | {'yes' if pl['vector_io'] else 'no'} | {tf:.0f} |")
+        log(lines[-1])
+    lines.append("")
     open(out_path, "w").write("\n".join(lines))
     print("\n".join(lines))
 
@@ -381,6 +446,10 @@ def main():
     ap.add_argument("--sweep", default=None,
                     help="run the M=2304, K=4096 N-sweep, write its summary to this file, then exit")
     ap.add_argument("--sweep-step", type=int, default=8)
+    ap.add_argument("--sweep-tune", action="store_true",
+                    help="with --sweep: also time tg_autotune's best plan at every point")
+    ap.add_argument("--align-sweep", default=None,
+                    help="run the K-alignment sweep, write its summary to this file, then exit")
     ap.add_argument("--traffic-kernel", default=None,
                     help="run one workload (or 'copy') for a rocprofv3 counter pass, then exit")
     ap.add_argument("--traffic-summarize", default=None,
@@ -408,7 +477,10 @@ def main():
         traffic_kernel(args.traffic_kernel)
         return
     if args.sweep:
-        sweep(args.sweep, args.sweep_step)
+        sweep(args.sweep, args.sweep_step, tune=args.sweep_tune)
+        return
+    if args.align_sweep:
+        align_sweep(args.align_sweep)
         return
     log("device", torch.cuda.get_device_name(0), "cus", tg.tg_device_cus())
 

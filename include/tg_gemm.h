@@ -172,6 +172,30 @@ int tg_plan_model(int64_t M, int64_t N, int64_t K, int dtype, int trans,
 size_t tg_workspace_size(int64_t M, int64_t N, int64_t K, int dtype, int trans,
                          const tg_options *opts);
 
+/* Benchmark mode ("Matrix Multiplication Background User's Guide", section
+ * 2.3: a library may time its candidate kernels instead of trusting its
+ * heuristic).  Runs the call once per candidate plan -- the planner's own
+ * choice, every macro tile the kernels offer for these operands with K split
+ * 1, 2, 3, 4, 6 or 8 ways, and the skinny path split 1, 2 or 4 ways when it
+ * applies -- each timed `reps` times (>= 1) after one warm-up with events on
+ * `stream`, and writes the fastest to *best (ready for tg_gemm_ex) and its
+ * mean time in microseconds to *best_us (may be NULL).
+ *
+ * C is overwritten by every run with the product under `epilogue`'s kind and
+ * slope; its alpha and beta are not applied while timing (beta would feed
+ * each run's C into the next).  Blocks until the timing is done.  workspace
+ * as for tg_gemm_ex (NULL: allocations are made per run).  Plans that need
+ * more workspace than given are skipped.  Returns a tg_status. */
+int tg_autotune(int64_t M, int64_t N, int64_t K,
+                const void *A, int64_t lda,
+                const void *B, int64_t ldb,
+                void *C, int64_t ldc,
+                int dtype, int trans,
+                const tg_epilogue *epilogue,
+                void *workspace, size_t workspace_bytes,
+                void *stream, int reps,
+                tg_options *best, float *best_us);
+
 /* Compute units of the current device, or a negative tg_status. */
 int tg_device_cus(void);
 

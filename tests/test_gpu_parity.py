@@ -385,3 +385,25 @@ def test_beta_needs_the_old_c():
     with pytest.raises(tg.TgError):
         tg.gemm(A, A, out=C, epilogue=bad)
 
+
+# ---------------------------------------------------------------- benchmark mode
+
+@pytest.mark.parametrize("shape", [(2304, 2048, 4096, NN), (1024, 128, 2048, NN), (520, 296, 264, NT)])
+def test_autotune_choice_is_valid_and_correct(shape):
+    """tg_autotune returns options tg_gemm_ex accepts, no slower than the
+    planner's own choice on the same timing, and the product under them
+    matches the oracle."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    M, N, K, trans = shape
+    _say("case autotune", shape)
+    p = make_problem(M, N, K, F16, trans, "normal", seed=41)
+    A = to_device(p.A, p.dtype)
+    B = to_device(p.B, p.dtype)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda:0")
+    opts, us = tg.autotune(A, B, trans_a=p.trans_a, trans_b=p.trans_b, workspace=ws, reps=3)
+    assert us > 0
+    assert opts["path"] in (tg.TG_PATH_AUTO, tg.TG_PATH_MFMA, tg.TG_PATH_SKINNY)
+    r, _, _ = check_full(p, options=None if opts["path"] == tg.TG_PATH_AUTO else opts, workspace=ws)
+    assert r["ok"], (opts, r)
+

@@ -79,6 +79,9 @@ def load():
     lib.tg_gemm_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, i32, ep, op, vp,
                                ctypes.c_size_t, vp]
     lib.tg_gemm_ex.restype = i32
+    lib.tg_autotune.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, i32, ep, vp,
+                                ctypes.c_size_t, vp, i32, op, ctypes.POINTER(ctypes.c_float)]
+    lib.tg_autotune.restype = i32
     lib.tg_gemm_plan.argtypes = [i64, i64, i64, i32, i32, op, pp]
     lib.tg_gemm_plan.restype = i32
     lib.tg_plan_model.argtypes = [i64, i64, i64, i32, i32, i32, i32, op, pp]
@@ -237,6 +240,33 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, o
                            dtype, trans, epi, _opts(options), ws_ptr, ws_bytes, stream)
     _check(rc)
     return out
+
+
+def autotune(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, out=None,
+             workspace=None, reps: int = 5, stream=None) -> tuple[dict, float]:
+    """Time every candidate plan for these operands (tg_autotune) and return
+    (options for ``gemm``, mean microseconds of the fastest).  ``out`` (or a
+    scratch tensor) is overwritten."""
+    import torch
+    dtype = _torch_dtype_code(A)
+    M, K = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
+    N = B.shape[0] if trans_b else B.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    trans = (TG_TRANS_A if trans_a else 0) | (TG_TRANS_B if trans_b else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    ws_ptr, ws_bytes = (None, 0)
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    best = Options(TG_PATH_AUTO, 0, 0, 0)
+    us = ctypes.c_float(0.0)
+    _check(load().tg_autotune(M, N, K, A.data_ptr() if A.numel() else None, _ld(A),
+                              B.data_ptr() if B.numel() else None, _ld(B), out.data_ptr(), _ld(out),
+                              dtype, trans, _epi(epilogue), ws_ptr, ws_bytes, stream, int(reps),
+                              ctypes.byref(best), ctypes.byref(us)))
+    opts = dict(path=best.path, tile_m=best.tile_m, tile_n=best.tile_n, split_k=best.split_k)
+    return opts, float(us.value)
 
 
 def plan_for(A, B, *, trans_a=False, trans_b=False, options=None) -> dict:

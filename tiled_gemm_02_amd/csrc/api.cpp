@@ -8,6 +8,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/tg_gemm.h"
 #include "kernels/launch.hpp"
@@ -528,6 +529,98 @@ size_t tg_workspace_size(int64_t M, int64_t N, int64_t K, int dtype, int trans,
     if (tg_gemm_plan(M, N, K, dtype, trans, opts, &pl) != TG_OK)
         return 0;
     return (size_t)pl.workspace_bytes;
+}
+
+int tg_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                int64_t ldb, void *C, int64_t ldc, int dtype, int trans,
+                const tg_epilogue *epilogue, void *workspace, size_t workspace_bytes, void *stream,
+                int reps, tg_options *best, float *best_us)
+{
+    if (!best)
+        return fail(TG_ERR_NULL, "best is NULL");
+    if (reps < 1)
+        return fail(TG_ERR_ARG, "reps=%d < 1", reps);
+    int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue);
+    if (rc != TG_OK)
+        return rc;
+    *best = tg_options{TG_PATH_AUTO, 0, 0, 0};
+    if (best_us)
+        *best_us = 0.0f;
+    if (M == 0 || N == 0 || K == 0)
+        return ok();   // nothing to choose
+    DeviceInfo *dev = nullptr;
+    rc = current_device(&dev);
+    if (rc != TG_OK)
+        return rc;
+    // timing runs: the epilogue's kind and slope, no alpha / beta
+    tg_epilogue epi{};
+    if (epilogue) {
+        epi.kind = epilogue->kind;
+        epi.slope = epilogue->slope;
+    }
+    // candidates: the planner's choice, then forced tiles and splits
+    std::vector<tg_options> cands;
+    cands.push_back(tg_options{TG_PATH_AUTO, 0, 0, 0});
+    const TileSpec *menu;
+    const int nmenu = tile_menu(dtype, &menu);
+    const int splits[] = {1, 2, 3, 4, 6, 8};
+    for (int i = 0; i < nmenu; ++i)
+        for (int sp : splits)
+            cands.push_back(tg_options{TG_PATH_MFMA, menu[i].bm, menu[i].bn, sp});
+    cands.push_back(tg_options{TG_PATH_MFMA, 64, 64, 1});   // the element-wise tile
+    for (int sp : {1, 2, 4})
+        cands.push_back(tg_options{TG_PATH_SKINNY, 0, 0, sp});
+
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0)
+            (void)hipEventDestroy(e0);
+        return fail(TG_ERR_DEVICE, "hipEventCreate failed");
+    }
+    const bool aligned = aligned16(A) && aligned16(B);
+    Problem p = make_problem(M, N, K, dtype, trans, lda, ldb, ldc, aligned);
+    Chip chip = device_chip(*dev);
+    float best_t = -1.0f;
+    int status = TG_OK;
+    for (const tg_options &o : cands) {
+        // skip candidates with no kernel for these operands, or without room
+        tg_plan pl;
+        const char *why = "";
+        if (make_plan(p, chip, 0, &o, device_occ, dev, false, &pl, &why) != TG_OK)
+            continue;
+        if (o.path != TG_PATH_AUTO && o.split_k > 1 && pl.split_k != o.split_k)
+            continue;   // the split collapsed to another candidate
+        if (workspace && pl.workspace_bytes > workspace_bytes)
+            continue;
+        if (gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, &epi, &o, workspace,
+                      workspace_bytes, stream) != TG_OK)
+            continue;   // e.g. a forced split that found no workspace
+        bool okrun = hipEventRecord(e0, s) == hipSuccess;
+        for (int r = 0; r < reps && okrun; ++r)
+            okrun = gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, &epi, &o, workspace,
+                              workspace_bytes, stream) == TG_OK;
+        okrun = okrun && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+        float ms = 0.0f;
+        if (!okrun || hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+            status = fail(TG_ERR_DEVICE, "timing a candidate failed");
+            break;
+        }
+        const float us = ms * 1000.0f / (float)reps;
+        if (best_t < 0.0f || us < best_t) {
+            best_t = us;
+            *best = o;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (status != TG_OK)
+        return status;
+    if (best_t < 0.0f)
+        return fail(TG_ERR_UNSUPPORTED, "no candidate plan ran");
+    if (best_us)
+        *best_us = best_t;
+    return ok();
 }
 
 int tg_device_cus(void)
