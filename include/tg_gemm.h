@@ -119,7 +119,9 @@ typedef struct tg_plan {
     int32_t split_k;     /* K-splits (1 = none) */
     int32_t occupancy;   /* workgroups resident per compute unit */
     int32_t num_cus;     /* compute units the wave model used */
-    int32_t vector_io;   /* 1 = 128-bit operand loads, 0 = element-wise */
+    int32_t vector_io;   /* 1 = 128-bit operand loads, 0 = element-wise, 2 = A and B first
+                            copied into zero-padded 16-byte-aligned buffers at the start of
+                            the workspace (K rounded up to 16 bytes), then 128-bit loads */
     int64_t tiles;       /* ceil(M/tile_m) * ceil(N/tile_n) */
     int64_t workgroups;  /* tiles * split_k (MFMA/skinny), or the GEMV grid */
     int64_t waves;       /* ceil(workgroups / (num_cus * occupancy)) */
@@ -131,9 +133,11 @@ typedef struct tg_plan {
     uint64_t workspace_bytes; /* float32 split-K partials the plan needs */
 } tg_plan;
 
-/* C = epi(A . B) on the current HIP device.  epilogue may be NULL (none).
- * When the plan splits K, float32 partials live in a stream-ordered
- * allocation made and released by the library on `stream`. */
+/* C = epi(alpha A . B + beta C) on the current HIP device.  epilogue may be
+ * NULL (C = A . B).  When the plan needs workspace (float32 split-K partials,
+ * or aligned copies of A and B), it is a stream-ordered allocation on
+ * `stream` from a memory pool the library keeps per device: memory a call
+ * frees stays reserved for later calls until the process ends. */
 int tg_gemm(int64_t M, int64_t N, int64_t K,
             const void *A, int64_t lda,
             const void *B, int64_t ldb,

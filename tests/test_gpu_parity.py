@@ -407,3 +407,40 @@ def test_autotune_choice_is_valid_and_correct(shape):
     r, _, _ = check_full(p, options=None if opts["path"] == tg.TG_PATH_AUTO else opts, workspace=ws)
     assert r["ok"], (opts, r)
 
+
+# ---------------------------------------------------------------- aligned copies
+#
+# Operands off the 16-byte grid (K odd, padded leading dimensions) in products
+# large enough to copy them into aligned buffers first.
+
+ALIGN_CASES = [
+    # M, N, K, dtype, trans, ld_pad
+    (1024, 1024, 521, F16, NN, 0),
+    (1024, 512, 1031, BF16, TN, 3),
+    (512, 1024, 1029, F16, NT, 1),
+    (1024, 512, 1030, BF16, TT, 5),
+    (1024, 512, 1027, F32, NN, 1),
+]
+
+
+@pytest.mark.parametrize("case", ALIGN_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}-p{c[5]}")
+def test_unaligned_operands_copied(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, dtype, trans, pad = case
+    _say("case aligned copy", case)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=51, ld_pad=pad)
+    assert tg.tg_plan_model(M, N, K, dtype, trans)["vector_io"] == 2
+    r, _, _ = check_full(p)
+    assert r["ok"], (case, r)
+    r, _, _ = check_scaled(p, 0.5, -1.0, epilogue="leaky_relu", c_seed=6)
+    assert r["ok"], (case, r)
+
+
+def test_unaligned_copy_with_a_small_workspace_falls_back():
+    """A caller workspace too small for the copies: the element-wise kernel runs."""
+    import torch
+    p = make_problem(1024, 1024, 521, F16, NN, "uniform", seed=52)
+    small = torch.empty(4096, dtype=torch.uint8, device="cuda:0")
+    r, _, _ = check_full(p, workspace=small)
+    assert r["ok"], r
+

@@ -110,3 +110,21 @@ def test_flop_formula_against_page_numbers():
     flop = 2 * 8192 * 4096 * 6144
     assert flop / 130.7831e-3 / 1e12 == pytest.approx(3.1533, rel=2e-3)
     assert flop / 261.9420e-3 / 1e12 == pytest.approx(1.5741, rel=1e-3)
+
+
+def test_unaligned_operands_are_copied_when_it_pays():
+    """K (or a leading dimension) off the 16-byte grid: a large product plans
+    an aligned, zero-padded copy of A and B (vector_io 2) with the copies at the
+    start of the workspace; a small one keeps the element-wise kernel."""
+    F = tg.TG_F16
+    big = tg.tg_plan_model(4096, 4096, 4097, F, tg.TG_NN)
+    assert big["vector_io"] == 2 and big["path_name"] == "mfma"
+    kp = 4104   # K rounded up to 8 elements
+    copies = 4096 * kp * 2 + kp * 4096 * 2
+    assert big["workspace_bytes"] >= copies
+    assert tg.tg_plan_model(4096, 4096, 4096, F, tg.TG_NN)["vector_io"] == 1
+    small = tg.tg_plan_model(64, 64, 65, F, tg.TG_NN)
+    assert small["vector_io"] == 0 and small["workspace_bytes"] == 0
+    # M or N off the grid: no copy (the padded product would write past C)
+    assert tg.tg_plan_model(4097, 4096, 4097, F, tg.TG_NN)["vector_io"] == 0
+

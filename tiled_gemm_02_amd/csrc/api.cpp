@@ -92,6 +92,17 @@ hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, i
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_pack(int dtype, const void *src, int64_t lds, int64_t rows, int64_t cols, void *dst,
+                       int64_t drows, int64_t dcols, hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F16: return launch_pack_f16(src, lds, rows, cols, dst, drows, dcols, s);
+    case TG_BF16: return launch_pack_bf16(src, lds, rows, cols, dst, drows, dcols, s);
+    case TG_F32: return launch_pack_f32(src, lds, rows, cols, dst, drows, dcols, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_scale_c(int dtype, void *C, int M, int N, int64_t ldc, const OutEpi &oe,
                           hipStream_t s)
 {
@@ -149,7 +160,13 @@ struct DeviceInfo {
     bool probed = false;
     bool gfx950 = false;
     int cus = 0;
+    int id = -1;
     std::string arch;
+    // workspace pool: memory freed by a call stays reserved for the next one
+    // (the device's default pool returns it at every synchronisation, and
+    // mapping tens of MiB again costs more than the split or copy it serves)
+    hipMemPool_t pool = nullptr;
+    bool pool_tried = false;
     // measured residency per (dtype, trans, tile, vec), 0 = not yet asked
     int occ[3][4][8][2] = {};
 };
@@ -177,6 +194,7 @@ static int current_device(DeviceInfo **info)
         d.arch = prop.gcnArchName;
         d.gfx950 = d.arch.compare(0, 6, "gfx950") == 0;
         d.cus = prop.multiProcessorCount;
+        d.id = dev;
         d.probed = true;
     }
     if (!d.gfx950)
@@ -184,6 +202,34 @@ static int current_device(DeviceInfo **info)
                     d.arch.c_str());
     *info = &d;
     return TG_OK;
+}
+
+// Stream-ordered workspace from the device's library pool (created on first
+// use, release threshold unlimited: the pool keeps its peak size until the
+// process ends), or from the default pool if no pool can be made.
+static hipError_t ws_alloc(DeviceInfo *d, void **ptr, size_t bytes, hipStream_t s)
+{
+    {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        if (!d->pool_tried) {
+            d->pool_tried = true;
+            hipMemPoolProps props{};
+            props.allocType = hipMemAllocationTypePinned;
+            props.location.type = hipMemLocationTypeDevice;
+            props.location.id = d->id;
+            hipMemPool_t pool = nullptr;
+            if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+                uint64_t keep = UINT64_MAX;
+                if (hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep) == hipSuccess)
+                    d->pool = pool;
+                else
+                    (void)hipMemPoolDestroy(pool);
+            }
+        }
+    }
+    if (d->pool)
+        return hipMallocFromPoolAsync(ptr, bytes, d->pool, s);
+    return hipMallocAsync(ptr, bytes, s);
 }
 
 static int tile_slot(int bm, int bn)
@@ -429,29 +475,59 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
     void *ws = nullptr;
     bool own_ws = false;
     if (pl.workspace_bytes > 0) {
+        if (user_ws && ((uintptr_t)user_ws & 255u) != 0)
+            return fail(TG_ERR_ARG, "workspace must be 256-byte aligned");
         if (user_ws) {
-            if (((uintptr_t)user_ws & 255u) != 0)
-                return fail(TG_ERR_ARG, "workspace must be 256-byte aligned");
-            if (user_ws_bytes >= pl.workspace_bytes) {
+            if (user_ws_bytes >= pl.workspace_bytes)
                 ws = user_ws;
-            }
+        } else if (ws_alloc(dev, &ws, pl.workspace_bytes, s) == hipSuccess) {
+            own_ws = true;
         } else {
-            hipError_t e = hipMallocAsync(&ws, pl.workspace_bytes, s);
-            if (e == hipSuccess)
-                own_ws = true;
-            else
-                ws = nullptr;
+            ws = nullptr;
         }
         if (!ws) {
             if (opts && opts->split_k > 1)
                 return fail(TG_ERR_ARG, "forced split_k=%d needs %llu bytes of workspace",
                             opts->split_k, (unsigned long long)pl.workspace_bytes);
+            // without the room: no K split, then no aligned copies either
             tg_options o = opts ? *opts : tg_options{TG_PATH_AUTO, 0, 0, 0};
             o.split_k = 1;
             rc = make_plan(p, chip, 0, &o, device_occ, dev, false, &pl, &why);
             if (rc != TG_OK)
                 return fail(rc, "%s", why);
+            if (pl.workspace_bytes > 0 && user_ws && user_ws_bytes >= pl.workspace_bytes) {
+                ws = user_ws;
+            } else if (pl.workspace_bytes > 0) {
+                rc = make_plan(p, chip, 0, &o, device_occ, dev, false, &pl, &why, false);
+                if (rc != TG_OK)
+                    return fail(rc, "%s", why);
+            }
         }
+    }
+    if (pl.vector_io == 2) {
+        // copy A and B into zero-padded aligned buffers, then run the aligned plan
+        const PackLayout L = pack_layout(p);
+        const Problem q = packed_problem(p);
+        const bool ta = trans & TG_TRANS_A, tb = trans & TG_TRANS_B;
+        char *w = (char *)ws;
+        hipError_t e = launch_pack(dtype, A, lda, ta ? K : M, ta ? M : K, w + L.a_off, L.a_rows,
+                                   L.a_cols, s);
+        if (e == hipSuccess)
+            e = launch_pack(dtype, B, ldb, tb ? N : K, tb ? K : N, w + L.b_off, L.b_rows, L.b_cols,
+                            s);
+        if (e != hipSuccess) {
+            if (own_ws)
+                (void)hipFreeAsync(ws, s);
+            return fail(TG_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+        }
+        tg_plan inner = pl;
+        inner.vector_io = 1;
+        rc = run_plan(inner, q, w + L.a_off, w + L.b_off, C, epi, w + L.bytes, s);
+        if (own_ws)
+            (void)hipFreeAsync(ws, s);
+        if (rc != TG_OK)
+            return rc;
+        return ok();
     }
     rc = run_plan(pl, p, A, B, C, epi, ws, s);
     if (own_ws)

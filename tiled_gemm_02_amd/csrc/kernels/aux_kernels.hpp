@@ -1,6 +1,8 @@
 // aux_kernels.hpp -- split-K reduction and the K == 0 / alpha == 0 output pass.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace tg {
@@ -72,6 +74,33 @@ __global__ __launch_bounds__(256) void scale_c_kernel(void *C_, int M, int N, in
         T *c = C + (int64_t)m * ldc + n;
         const float c_old = oe.beta != 0.0f ? Tr::to_f32(*c) : 0.0f;
         *c = Tr::from_f32(apply_epi(oe.beta != 0.0f ? oe.beta * c_old : 0.0f, oe.kind, oe.slope));
+    }
+}
+
+// Aligned copy of one operand: dst (drows x dcols, row-major, ld = dcols, a
+// multiple of 16 bytes) gets src (rows x cols, ld = lds, any alignment) in
+// its top-left corner and zeros elsewhere.  Zero rows and columns past K add
+// nothing to the product.  One thread per 16-byte chunk of dst.
+template <typename Tr>
+__global__ __launch_bounds__(256) void pack_kernel(const void *src_, int64_t lds, int64_t rows,
+                                                   int64_t cols, void *dst_, int64_t drows,
+                                                   int64_t dcols)
+{
+    using W = std::conditional_t<Tr::kBytes == 2, uint16_t, uint32_t>;   // the stored bits
+    constexpr int E = 16 / Tr::kBytes;
+    const W *src = (const W *)src_;
+    W *dst = (W *)dst_;
+    const int64_t cpr = dcols / E;
+    const int64_t total = drows * cpr;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t r = idx / cpr;
+        const int64_t c0 = (idx - r * cpr) * E;
+        W v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            v[e] = (r < rows && c0 + e < cols) ? src[r * lds + c0 + e] : (W)0;
+        *(u32x4 *)(dst + r * dcols + c0) = __builtin_bit_cast(u32x4, v);
     }
 }
 

@@ -21,6 +21,9 @@ hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a,
 int mfma2_occupancy(int dtype, int trans, int bm, int bn);
 hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, int N, void *C,
                                 int64_t ldc, const OutEpi &oe, int c_vec, hipStream_t s);
+// Aligned, zero-padded copy of a rows x cols operand into drows x dcols.
+hipError_t launch_pack(int dtype, const void *src, int64_t lds, int64_t rows, int64_t cols, void *dst,
+                       int64_t drows, int64_t dcols, hipStream_t s);
 // C = epi(beta * C): K == 0 or alpha == 0.
 hipError_t launch_scale_c(int dtype, void *C, int M, int N, int64_t ldc, const OutEpi &oe,
                           hipStream_t s);
@@ -37,6 +40,8 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
     int mfma_occupancy_##NAME(int trans, int bm, int bn, bool vec);                              \
     hipError_t launch_splitk_reduce_##NAME(const float *ws, int splits, int M, int N, void *C,   \
                                            int64_t ldc, OutEpi oe, int c_vec, hipStream_t s);    \
+    hipError_t launch_pack_##NAME(const void *src, int64_t lds, int64_t rows, int64_t cols,      \
+                                  void *dst, int64_t drows, int64_t dcols, hipStream_t s);       \
     hipError_t launch_scale_c_##NAME(void *C, int M, int N, int64_t ldc, OutEpi oe,             \
                                      hipStream_t s);                                             \
     hipError_t launch_gemv_##NAME(bool rows_form, bool vec, int lpr, const GemvArgs &a,          \

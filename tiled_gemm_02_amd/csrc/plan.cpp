@@ -400,8 +400,50 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
 
 // ---------------------------------------------------------------- entry
 
+// ---------------------------------------------------------------- aligned copies
+
+static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+Problem packed_problem(const Problem &p)
+{
+    const int E = chunk_elems(p.dtype);
+    Problem q = p;
+    q.K = round_up(p.K, E);
+    q.lda = (p.trans & TG_TRANS_A) ? p.M : q.K;
+    q.ldb = (p.trans & TG_TRANS_B) ? q.K : p.N;
+    q.ptrs_aligned = true;
+    return q;
+}
+
+PackLayout pack_layout(const Problem &p)
+{
+    const Problem q = packed_problem(p);
+    const int64_t es = elem_bytes(p.dtype);
+    PackLayout L;
+    const bool ta = p.trans & TG_TRANS_A, tb = p.trans & TG_TRANS_B;
+    L.a_rows = ta ? q.K : p.M;
+    L.a_cols = ta ? p.M : q.K;
+    L.b_rows = tb ? p.N : q.K;
+    L.b_cols = tb ? q.K : p.N;
+    L.a_off = 0;
+    L.b_off = (uint64_t)round_up(L.a_rows * L.a_cols * es, 256);
+    L.bytes = L.b_off + (uint64_t)round_up(L.b_rows * L.b_cols * es, 256);
+    return L;
+}
+
+// Worth copying: the element-wise kernel runs at a few percent of the vector
+// ones, so above about 1 GFLOP (20 us of element-wise work) the copies (two
+// short launches and one pass over A and B) pay for themselves many times.
+static bool pack_worthwhile(const Problem &p)
+{
+    const int E = chunk_elems(p.dtype);
+    return p.M > 1 && p.N > 1 && p.M % E == 0 && p.N % E == 0 &&
+           2.0 * (double)p.M * (double)p.N * (double)p.K >= 1e9;
+}
+
 int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_options *opts,
-              OccFn occ, void *occ_ctx, bool model, tg_plan *out, const char **why)
+              OccFn occ, void *occ_ctx, bool model, tg_plan *out, const char **why,
+              bool allow_pack)
 {
     static const char *none = "";
     *why = none;
@@ -428,6 +470,24 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
         out->path = TG_PATH_NONE;
         out->pred_us = 0.0;
         return TG_OK;
+    }
+    if (allow_pack && !vec_ok(p) && pack_worthwhile(p) && !(opts && opts->path == TG_PATH_GEMV)) {
+        // plan the padded, aligned copy ("Matrix Multiplication Background
+        // User's Guide", section 3.1: multiples of 8 elements keep the matrix
+        // units fed; padding is how a caller gets there)
+        const Problem q = packed_problem(p);
+        tg_plan inner;
+        const int rc = make_plan(q, chip, occupancy, opts, occ, occ_ctx, model, &inner, why, false);
+        if (rc == TG_OK && inner.vector_io == 1) {
+            const PackLayout L = pack_layout(p);
+            *out = inner;
+            out->vector_io = 2;
+            out->workspace_bytes = L.bytes + inner.workspace_bytes;
+            out->pred_us += 2.0 * (double)L.bytes / (chip.hbm_gbs * 1e3) + 2.0 * chip.launch_us;
+            fill_common(p, chip, out);
+            return TG_OK;
+        }
+        *why = "";
     }
     int path = opts ? opts->path : TG_PATH_AUTO;
     if (path == TG_PATH_AUTO && opts && (opts->tile_m > 0 || opts->tile_n > 0))

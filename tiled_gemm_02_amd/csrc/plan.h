@@ -63,7 +63,23 @@ typedef int (*OccFn)(int dtype, int trans, int bm, int bn, bool vec, void *ctx);
 // Returns TG_OK or a tg_status; `why` receives a static description on error.
 // model: called from the pure model, which may price tiles no kernel offers.
 int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_options *opts,
-              OccFn occ, void *occ_ctx, bool model, tg_plan *out, const char **why);
+              OccFn occ, void *occ_ctx, bool model, tg_plan *out, const char **why,
+              bool allow_pack = true);
+
+// Operands that cannot take 16-byte loads (K, a leading dimension or a base
+// pointer not 16-byte aligned) are copied, when the product is large enough,
+// into zero-padded aligned buffers at the start of the workspace (plan
+// vector_io == 2).  PackLayout describes those buffers; packed_problem() is
+// the problem the kernels then see (K rounded up to 16 bytes, packed leading
+// dimensions, aligned).
+struct PackLayout {
+    int64_t a_rows, a_cols;   // stored A' (row-major): (trans_a ? K' x M : M x K')
+    int64_t b_rows, b_cols;   // stored B': (trans_b ? N x K' : K' x N)
+    uint64_t a_off, b_off;    // byte offsets in the workspace
+    uint64_t bytes;           // both buffers; the kernels' own workspace follows
+};
+PackLayout pack_layout(const Problem &p);
+Problem packed_problem(const Problem &p);
 
 // 16-byte-chunk element count of a storage type.
 inline int chunk_elems(int dtype) { return dtype == TG_F32 ? 4 : 8; }
