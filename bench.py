@@ -392,22 +392,27 @@ def sweep(out_path: str, step: int, reps: int = 5, tune: bool = False):
 
 
 def align_sweep(out_path: str, reps: int = 5):
-    """fp16 NN M = N = 4096, K = 4096 + d for d = 0 .. 16: 16-byte-aligned rows (d % 8 == 0)
-    take the LDS-DMA kernels, the others the element-wise load path (the K-alignment
-    effect of "Matrix Multiplication Background User's Guide", section 3.1)."""
+    """fp16 NN products of about 4096^3 with one size off the 16-byte grid: K = 4096 + d
+    (rows of A off the grid) and M = N = 4096 + d (ragged tiles and rows of B and C off
+    the grid) for d = 0 .. 16 (the alignment effect of "Matrix Multiplication Background
+    User's Guide", section 3.1).  Aligned sizes take the LDS-DMA kernels directly, the
+    others aligned copies (staged in float32 when M or N is off the grid)."""
     import torch
     import tiled_gemm_02_amd as tg
-    from gemm_inputs import F16, NN
     device = torch.device("cuda:0")
-    M = N = 4096
     stream = torch.cuda.current_stream(device)
     g = torch.Generator(device=device).manual_seed(6)
-    lines = ["# K-alignment sweep: fp16 NN, M = N = 4096, K = 4096 + d", "",
+    lines = ["# Alignment sweep: fp16 NN, one size off the 16-byte grid", "",
              "Command (repository root, one MI355X):", "", "```",
              f"python3 bench.py --align-sweep {out_path}", "```", "",
-             "| K | K mod 8 | Path | Tile | Split | Vector loads | TFLOP/s |", "|---|---|---|---|---|---|---|"]
-    for d in range(17):
-        K = 4096 + d
+             "Loads: vector = 128-bit loads of the caller's operands, copied = aligned",
+             "zero-padded copies first (padded in M and N too where those are off the grid;",
+             "the kernel then stores only the M x N corner).", "",
+             "| M | N | K | Path | Tile | Split | Loads | us | TFLOP/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    shapes = [(4096, 4096, 4096 + d) for d in range(17)] + \
+             [(4096 + d, 4096 + d, 4096) for d in range(1, 17)]
+    for M, N, K in shapes:
         A = (torch.randn((M, K), generator=g, device=device) / math.sqrt(K)).half()
         B = (torch.randn((K, N), generator=g, device=device) / math.sqrt(K)).half()
         C = torch.empty((M, N), dtype=torch.float16, device=device)
@@ -424,9 +429,10 @@ def align_sweep(out_path: str, reps: int = 5):
             ts.append(e0.elapsed_time(e1))
         ms = sorted(ts)[len(ts) // 2]
         tf = 2.0 * M * N * K / ms / 1e9
+        loads = {0: "element-wise", 1: "vector", 2: "copied"}[pl["vector_io"]]
         # plan_for assumes packed operands; the real call sees the same strides here
-        lines.append(f"| {K} | {K % 8} | {pl['path_name']} | {pl['tile_m']}x{pl['tile_n']} | "
-                     f"{pl['split_k']} | {'yes' if pl['vector_io'] else 'no'} | {tf:.0f} |")
+        lines.append(f"| {M} | {N} | {K} | {pl['path_name']} | {pl['tile_m']}x{pl['tile_n']} | "
+                     f"{pl['split_k']} | {loads} | {ms * 1e3:.0f} | {tf:.0f} |")
         log(lines[-1])
     lines.append("")
     open(out_path, "w").write("\n".join(lines))

@@ -436,6 +436,44 @@ def test_unaligned_operands_copied(case):
     assert r["ok"], (case, r)
 
 
+# M or N off the grid as well: the copies are padded in M and N too and the
+# macro-tile kernel stores only the M x N corner (ragged tails in every
+# dimension, padded C rows, scaled forms, a forced K split).
+PADDED_MN_CASES = [
+    # M, N, K, dtype, trans, ld_pad
+    (1025, 1000, 1031, F16, NN, 0),
+    (999, 1024, 1024, BF16, TN, 2),
+    (1024, 1003, 600, F16, NT, 0),
+    (517, 1021, 1000, BF16, TT, 1),
+    (1001, 1000, 999, F32, NN, 0),
+    (8191, 100, 1000, F16, NN, 0),
+]
+
+
+@pytest.mark.parametrize("case", PADDED_MN_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}-p{c[5]}")
+def test_unaligned_rows_and_columns_copied(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, dtype, trans, pad = case
+    _say("case padded copy", case)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=53, ld_pad=pad)
+    pl = tg.tg_plan_model(M, N, K, dtype, trans)
+    assert pl["vector_io"] == 2 and pl["path_name"] == "mfma"
+    r, _, _ = check_full(p, out_pad=3)
+    assert r["ok"], (case, r)
+    r, _, _ = check_scaled(p, 0.5, -1.0, epilogue="leaky_relu", c_seed=7)
+    assert r["ok"], (case, r)
+
+
+def test_padded_copy_with_forced_split():
+    p = make_problem(1025, 1000, 4100, F16, NN, "uniform", seed=54)
+    for split in (1, 3):
+        _say("case padded split", split)
+        r, _, _ = check_full(p, options=dict(split_k=split, tile_m=128, tile_n=128))
+        assert r["ok"], (split, r)
+        r, _, _ = check_scaled(p, 2.0, 0.5, options=dict(split_k=split), c_seed=8)
+        assert r["ok"], (split, r)
+
+
 def test_unaligned_copy_with_a_small_workspace_falls_back():
     """A caller workspace too small for the copies: the element-wise kernel runs."""
     import torch

@@ -112,6 +112,10 @@ def test_flop_formula_against_page_numbers():
     assert flop / 261.9420e-3 / 1e12 == pytest.approx(1.5741, rel=1e-3)
 
 
+def round256(x):
+    return (x + 255) // 256 * 256
+
+
 def test_unaligned_operands_are_copied_when_it_pays():
     """K (or a leading dimension) off the 16-byte grid: a large product plans
     an aligned, zero-padded copy of A and B (vector_io 2) with the copies at the
@@ -125,6 +129,21 @@ def test_unaligned_operands_are_copied_when_it_pays():
     assert tg.tg_plan_model(4096, 4096, 4096, F, tg.TG_NN)["vector_io"] == 1
     small = tg.tg_plan_model(64, 64, 65, F, tg.TG_NN)
     assert small["vector_io"] == 0 and small["workspace_bytes"] == 0
-    # M or N off the grid: no copy (the padded product would write past C)
-    assert tg.tg_plan_model(4097, 4096, 4097, F, tg.TG_NN)["vector_io"] == 0
+    # M or N off the grid too: the copies are padded to M' x K' and K' x N',
+    # and the macro-tile kernel (loads bounded by M', N', stores by M, N) runs it
+    padded = tg.tg_plan_model(4097, 4090, 4097, F, tg.TG_NN)
+    assert padded["vector_io"] == 2 and padded["path_name"] == "mfma"
+    mp, np_ = 4104, 4096
+    copies = round256(mp * kp * 2) + round256(kp * np_ * 2)
+    assert padded["workspace_bytes"] >= copies
+    assert padded["tiles"] == -(-4097 // padded["tile_m"]) * -(-4090 // padded["tile_n"])
+    # a narrow padded product leaves the skinny path for the macro-tile one
+    narrow = tg.tg_plan_model(8191, 100, 8191, F, tg.TG_NN)
+    assert narrow["vector_io"] == 2 and narrow["path_name"] == "mfma"
+    # a forced skinny path is not turned into a macro-tile product:
+    # with N off the grid it is unsupported, with only K off it is copied
+    with pytest.raises(tg.TgError):
+        tg.tg_plan_model(8191, 100, 8191, F, tg.TG_NN, options=dict(path="skinny"))
+    sk = tg.tg_plan_model(8192, 96, 8191, F, tg.TG_NN, options=dict(path="skinny"))
+    assert sk["vector_io"] == 2 and sk["path_name"] == "skinny"
 

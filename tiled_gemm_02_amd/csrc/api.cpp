@@ -81,13 +81,14 @@ int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec)
     return 0;
 }
 
-hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, int N, void *C,
-                                int64_t ldc, const OutEpi &oe, int c_vec, hipStream_t s)
+hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int64_t wsld, int64_t plane,
+                                int M, int N, void *C, int64_t ldc, const OutEpi &oe, int c_vec,
+                                hipStream_t s)
 {
     switch (dtype) {
-    case TG_F16: return launch_splitk_reduce_f16(ws, splits, M, N, C, ldc, oe, c_vec, s);
-    case TG_BF16: return launch_splitk_reduce_bf16(ws, splits, M, N, C, ldc, oe, c_vec, s);
-    case TG_F32: return launch_splitk_reduce_f32(ws, splits, M, N, C, ldc, oe, c_vec, s);
+    case TG_F16: return launch_splitk_reduce_f16(ws, splits, wsld, plane, M, N, C, ldc, oe, c_vec, s);
+    case TG_BF16: return launch_splitk_reduce_bf16(ws, splits, wsld, plane, M, N, C, ldc, oe, c_vec, s);
+    case TG_F32: return launch_splitk_reduce_f32(ws, splits, wsld, plane, M, N, C, ldc, oe, c_vec, s);
     }
     return hipErrorInvalidValue;
 }
@@ -339,8 +340,11 @@ static OutEpi out_epi(const tg_epilogue *epi)
     return oe;
 }
 
+// rows_a, cols_b: rows of A and columns of B the macro-tile kernel may read
+// (0: M and N; zero-padded copies hold more, rounded up to whole 16-byte chunks).
 static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const void *B, void *C,
-                    const tg_epilogue *epi, void *ws, hipStream_t s)
+                    const tg_epilogue *epi, void *ws, hipStream_t s, int64_t rows_a = 0,
+                    int64_t cols_b = 0)
 {
     const OutEpi oe = out_epi(epi);
     const int E = chunk_elems(p.dtype);
@@ -371,12 +375,14 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.oe = oe;
         const int cb = elem_bytes(p.dtype);
         a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
+        a.rows_a = (int)(rows_a ? rows_a : p.M);
+        a.cols_b = (int)(cols_b ? cols_b : p.N);
         if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, p.M, p.N, p.K, p.lda, p.ldb))
             e = launch_mfma2(p.dtype, p.trans, pl.tile_m, pl.tile_n, a, s);
         else
             e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);
         if (e == hipSuccess && pl.split_k > 1)
-            e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, (int)p.M, (int)p.N, C,
+            e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, p.N, p.M * p.N, (int)p.M, (int)p.N, C,
                                      p.ldc, oe, a.c_vec, s);
     } else if (pl.path == TG_PATH_SKINNY) {
         SkinnyArgs a{};
@@ -402,7 +408,7 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
         e = launch_skinny(p.dtype, (p.trans & TG_TRANS_B) != 0, a, s);
         if (e == hipSuccess && pl.split_k > 1)
-            e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, (int)p.M, (int)p.N, C,
+            e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, p.N, p.M * p.N, (int)p.M, (int)p.N, C,
                                      p.ldc, oe, a.c_vec, s);
     } else if (pl.path == TG_PATH_GEMV) {
         const bool ta = p.trans & TG_TRANS_A, tb = p.trans & TG_TRANS_B;
@@ -463,6 +469,14 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
     if (rc != TG_OK)
         return rc;
     hipStream_t s = (hipStream_t)stream;
+    const OutEpi oe0 = out_epi(epi);
+    if (K == 0 || oe0.alpha == 0.0f) {
+        // no product term: C = epi(beta * C), A and B untouched (no plan, no workspace)
+        const hipError_t e = launch_scale_c(dtype, C, (int)M, (int)N, ldc, oe0, s);
+        if (e != hipSuccess)
+            return fail(TG_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
     const bool aligned = aligned16(A) && aligned16(B);
     Problem p = make_problem(M, N, K, dtype, trans, lda, ldb, ldc, aligned);
     Chip chip = device_chip(*dev);
@@ -522,7 +536,13 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
         }
         tg_plan inner = pl;
         inner.vector_io = 1;
-        rc = run_plan(inner, q, w + L.a_off, w + L.b_off, C, epi, w + L.bytes, s);
+        // the copies are read over their padded extent; the M x N result goes
+        // straight to C (rows and columns past M and N are computed from the
+        // zero padding and never stored)
+        Problem r = q;
+        r.M = M;
+        r.N = N;
+        rc = run_plan(inner, r, w + L.a_off, w + L.b_off, C, epi, w + L.bytes, s, q.M, q.N);
         if (own_ws)
             (void)hipFreeAsync(ws, s);
         if (rc != TG_OK)

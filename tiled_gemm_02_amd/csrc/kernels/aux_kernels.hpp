@@ -7,27 +7,30 @@
 
 namespace tg {
 
-// C[m][n] = out(sum_{z < splits} ws[z][m][n]), summed in increasing z so the
-// result does not depend on which split finished first.  Splitting K needs
+// C[m][n] = out(sum_{z < splits} ws[z * plane + m * wsld + n]), summed in
+// increasing z so the result does not depend on which split finished first
+// (the partials may be wider than C: padded products).  Splitting K needs
 // this final reduction ("Matrix Multiplication Background User's Guide",
 // section 2.3).  One thread per 4 consecutive outputs of a row.
 template <typename Tr>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ ws, int splits,
-                                                            int M, int N, void *C_, int64_t ldc,
-                                                            OutEpi oe, int c_vec)
+                                                            int64_t wsld, int64_t plane, int M, int N,
+                                                            void *C_, int64_t ldc, OutEpi oe,
+                                                            int c_vec)
 {
     using T = typename Tr::T;
     T *C = (T *)C_;
     const int nq = (N + 3) >> 2;
     const int64_t total = (int64_t)M * nq;
-    const int64_t plane = (int64_t)M * N;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * 256) {
         const int m = (int)(idx / nq);
         const int n = (int)(idx - (int64_t)m * nq) * 4;
-        const float *src = ws + (int64_t)m * N + n;
+        const float *src = ws + (int64_t)m * wsld + n;
         float s[4] = {0.f, 0.f, 0.f, 0.f};
-        const bool vec_in = (N & 3) == 0;
+        // a row of the sums holds wsld >= N floats, so with wsld and plane multiples
+        // of 4 a 4-float read at n < N stays inside it
+        const bool vec_in = (wsld & 3) == 0 && (plane & 3) == 0;
         // four splits per round: their loads are in flight together, the sum
         // still runs in increasing split order
         for (int z0 = 0; z0 < splits; z0 += 4) {

@@ -19,8 +19,10 @@ int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec);
 // The LDS-DMA kernel for 16-bit, 16-byte-aligned operands (same tiles).
 hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s);
 int mfma2_occupancy(int dtype, int trans, int bm, int bn);
-hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int M, int N, void *C,
-                                int64_t ldc, const OutEpi &oe, int c_vec, hipStream_t s);
+// C (M x N) = out(sum of `splits` float32 planes of partials, rows wsld apart)
+hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int64_t wsld, int64_t plane,
+                                int M, int N, void *C, int64_t ldc, const OutEpi &oe, int c_vec,
+                                hipStream_t s);
 // Aligned, zero-padded copy of a rows x cols operand into drows x dcols.
 hipError_t launch_pack(int dtype, const void *src, int64_t lds, int64_t rows, int64_t cols, void *dst,
                        int64_t drows, int64_t dcols, hipStream_t s);
@@ -38,8 +40,9 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
     hipError_t launch_mfma_##NAME(int trans, int bm, int bn, bool vec, const MfmaArgs &a,        \
                                   hipStream_t s);                                                \
     int mfma_occupancy_##NAME(int trans, int bm, int bn, bool vec);                              \
-    hipError_t launch_splitk_reduce_##NAME(const float *ws, int splits, int M, int N, void *C,   \
-                                           int64_t ldc, OutEpi oe, int c_vec, hipStream_t s);    \
+    hipError_t launch_splitk_reduce_##NAME(const float *ws, int splits, int64_t wsld,            \
+                                           int64_t plane, int M, int N, void *C, int64_t ldc,    \
+                                           OutEpi oe, int c_vec, hipStream_t s);                 \
     hipError_t launch_pack_##NAME(const void *src, int64_t lds, int64_t rows, int64_t cols,      \
                                   void *dst, int64_t drows, int64_t dcols, hipStream_t s);       \
     hipError_t launch_scale_c_##NAME(void *C, int M, int N, int64_t ldc, OutEpi oe,             \

@@ -49,6 +49,8 @@ struct MfmaArgs {
     int tiles_m, tiles_n;
     OutEpi oe;        // output transform
     int c_vec;        // 1: C rows are 16-byte aligned and ldc % 4 == 0
+    int rows_a;       // rows of A(i, k) the loads may touch, >= M (padded copies: M rounded up)
+    int cols_b;       // columns of B(k, j) the loads may touch, >= N
 };
 
 // 16-byte-chunk XOR swizzle of an LDS row (8 chunks per row).
@@ -208,9 +210,9 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs p)
     const int nk = (kend - kbeg + BK - 1) / BK;
 
     Stager<Tr, BM, TA, VEC> sa;
-    sa.X = (const T *)p.A; sa.ld = p.lda; sa.rows_total = p.M; sa.row0 = m0;
+    sa.X = (const T *)p.A; sa.ld = p.lda; sa.rows_total = p.rows_a; sa.row0 = m0;
     Stager<Tr, BN, !TB, VEC> sb;
-    sb.X = (const T *)p.B; sb.ld = p.ldb; sb.rows_total = p.N; sb.row0 = n0;
+    sb.X = (const T *)p.B; sb.ld = p.ldb; sb.rows_total = p.cols_b; sb.row0 = n0;
 
     f32x4 acc[FM][FN];
 #pragma unroll

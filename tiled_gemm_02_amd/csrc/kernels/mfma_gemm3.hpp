@@ -305,8 +305,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
     const int nst = nfull + has_tail;             // stages processed
     OpA oa;
     OpB ob;
-    oa.init((const uint16_t *)p.A, p.lda, p.M, m0, kbeg, wave, lane);
-    ob.init((const uint16_t *)p.B, p.ldb, p.N, n0, kbeg, wave, lane);
+    oa.init((const uint16_t *)p.A, p.lda, p.rows_a, m0, kbeg, wave, lane);
+    ob.init((const uint16_t *)p.B, p.ldb, p.cols_b, n0, kbeg, wave, lane);
 
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
     // Load processing stage t into its buffer: the K-tail (stage 0 when there

@@ -121,9 +121,9 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
     OpA oa;
     OpB ob;
     if (grp == 0)
-        oa.init((const uint16_t *)p.A, p.lda, p.M, m0, kbeg, gwave, lane);
+        oa.init((const uint16_t *)p.A, p.lda, p.rows_a, m0, kbeg, gwave, lane);
     else
-        ob.init((const uint16_t *)p.B, p.ldb, p.N, n0, kbeg, gwave, lane);
+        ob.init((const uint16_t *)p.B, p.ldb, p.cols_b, n0, kbeg, gwave, lane);
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
     // this group's operand of processing stage t into its buffer: the K tail
     // (stage 0 when there is one) through registers, the rest by DMA

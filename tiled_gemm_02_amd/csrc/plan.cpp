@@ -408,9 +408,11 @@ Problem packed_problem(const Problem &p)
 {
     const int E = chunk_elems(p.dtype);
     Problem q = p;
+    q.M = round_up(p.M, E);
+    q.N = round_up(p.N, E);
     q.K = round_up(p.K, E);
-    q.lda = (p.trans & TG_TRANS_A) ? p.M : q.K;
-    q.ldb = (p.trans & TG_TRANS_B) ? q.K : p.N;
+    q.lda = (p.trans & TG_TRANS_A) ? q.M : q.K;
+    q.ldb = (p.trans & TG_TRANS_B) ? q.K : q.N;
     q.ptrs_aligned = true;
     return q;
 }
@@ -421,13 +423,14 @@ PackLayout pack_layout(const Problem &p)
     const int64_t es = elem_bytes(p.dtype);
     PackLayout L;
     const bool ta = p.trans & TG_TRANS_A, tb = p.trans & TG_TRANS_B;
-    L.a_rows = ta ? q.K : p.M;
-    L.a_cols = ta ? p.M : q.K;
-    L.b_rows = tb ? p.N : q.K;
-    L.b_cols = tb ? q.K : p.N;
+    L.a_rows = ta ? q.K : q.M;
+    L.a_cols = ta ? q.M : q.K;
+    L.b_rows = tb ? q.N : q.K;
+    L.b_cols = tb ? q.K : q.N;
     L.a_off = 0;
     L.b_off = (uint64_t)round_up(L.a_rows * L.a_cols * es, 256);
     L.bytes = L.b_off + (uint64_t)round_up(L.b_rows * L.b_cols * es, 256);
+    L.padded_mn = q.M != p.M || q.N != p.N;
     return L;
 }
 
@@ -436,9 +439,7 @@ PackLayout pack_layout(const Problem &p)
 // short launches and one pass over A and B) pay for themselves many times.
 static bool pack_worthwhile(const Problem &p)
 {
-    const int E = chunk_elems(p.dtype);
-    return p.M > 1 && p.N > 1 && p.M % E == 0 && p.N % E == 0 &&
-           2.0 * (double)p.M * (double)p.N * (double)p.K >= 1e9;
+    return p.M > 1 && p.N > 1 && 2.0 * (double)p.M * (double)p.N * (double)p.K >= 1e9;
 }
 
 int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_options *opts,
@@ -476,10 +477,19 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
         // User's Guide", section 3.1: multiples of 8 elements keep the matrix
         // units fed; padding is how a caller gets there)
         const Problem q = packed_problem(p);
+        const PackLayout L = pack_layout(p);
         tg_plan inner;
-        const int rc = make_plan(q, chip, occupancy, opts, occ, occ_ctx, model, &inner, why, false);
+        int rc = make_plan(q, chip, occupancy, opts, occ, occ_ctx, model, &inner, why, false);
+        const bool forced_other = opts && opts->path != TG_PATH_AUTO && opts->path != TG_PATH_MFMA;
+        if (L.padded_mn && forced_other)
+            rc = TG_ERR_UNSUPPORTED;  // the forced path keeps its own element-wise form
+        else if (rc == TG_OK && L.padded_mn && inner.path != TG_PATH_MFMA) {
+            // only the macro-tile kernel reads past M and N
+            tg_options o = opts ? *opts : tg_options{TG_PATH_AUTO, 0, 0, 0};
+            o.path = TG_PATH_MFMA;
+            rc = make_plan(q, chip, occupancy, &o, occ, occ_ctx, model, &inner, why, false);
+        }
         if (rc == TG_OK && inner.vector_io == 1) {
-            const PackLayout L = pack_layout(p);
             *out = inner;
             out->vector_io = 2;
             out->workspace_bytes = L.bytes + inner.workspace_bytes;

@@ -66,17 +66,21 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
               OccFn occ, void *occ_ctx, bool model, tg_plan *out, const char **why,
               bool allow_pack = true);
 
-// Operands that cannot take 16-byte loads (K, a leading dimension or a base
-// pointer not 16-byte aligned) are copied, when the product is large enough,
-// into zero-padded aligned buffers at the start of the workspace (plan
+// Operands that cannot take 16-byte loads (M, N, K, a leading dimension or a
+// base pointer off the 16-byte grid) are copied, when the product is large
+// enough, into zero-padded aligned buffers at the start of the workspace (plan
 // vector_io == 2).  PackLayout describes those buffers; packed_problem() is
-// the problem the kernels then see (K rounded up to 16 bytes, packed leading
-// dimensions, aligned).
+// the problem the kernels then see (M, N and K rounded up to 16 bytes, packed
+// leading dimensions, aligned).  When M or N was rounded up only the
+// macro-tile kernel runs the product: it reads the copies over their padded
+// extent and stores the M x N result straight into C (its stores are bounded
+// by M and N, its loads by M' and N').
 struct PackLayout {
-    int64_t a_rows, a_cols;   // stored A' (row-major): (trans_a ? K' x M : M x K')
-    int64_t b_rows, b_cols;   // stored B': (trans_b ? N x K' : K' x N)
+    int64_t a_rows, a_cols;   // stored A' (row-major): (trans_a ? K' x M' : M' x K')
+    int64_t b_rows, b_cols;   // stored B': (trans_b ? N' x K' : K' x N')
     uint64_t a_off, b_off;    // byte offsets in the workspace
     uint64_t bytes;           // both buffers; the kernels' own workspace follows
+    bool padded_mn;           // M or N rounded up
 };
 PackLayout pack_layout(const Problem &p);
 Problem packed_problem(const Problem &p);
