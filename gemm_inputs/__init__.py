@@ -226,6 +226,83 @@ WORKLOADS = {
 }
 
 
+# ---------------------------------------------------------------- row softmax inputs
+#
+# Recipe: X (M x N, row-major, rows ld = N + ld_pad elements apart) drawn in
+# float64 from default_rng([seed, 11]); "normal": i.i.d. N(0, 1), the input of
+# the fused-softmax example on the Triton news page ("OpenAI open-sources
+# Triton", programming-model section, a 583 x 931 matrix from torch.normal);
+# "wide": N(0, 1) * 30, so that most exponentials of a row fall far below the
+# row maximum (and below the float32 and float16 normal ranges); "specials":
+# "normal" with a few rows overwritten by the degenerate cases the definition
+# has - a constant row, a row with some -inf entries, an all -inf row, a row
+# with a +inf entry, a row with a NaN entry, and a row of huge equal-magnitude
+# values (+-1e4) - at seeded row positions (see softmax_special_rows).  Rounded
+# to the storage type as the GEMM operands are.
+
+SPECIAL_ROWS = ("constant", "some_neg_inf", "all_neg_inf", "pos_inf", "nan", "huge")
+
+
+@dataclass
+class SoftmaxProblem:
+    """One row-softmax instance: stored X (M x ldx) plus the metadata the ABI needs."""
+    M: int
+    N: int
+    dtype: int
+    X: np.ndarray          # stored array, storage type (bfloat16 as uint16 bits)
+    ldx: int
+    desc: dict = field(default_factory=dict)
+
+
+def softmax_special_rows(M: int, seed: int) -> dict:
+    """Row index of each special case (distinct rows, seeded), for M >= len(SPECIAL_ROWS)."""
+    rng = np.random.default_rng([seed, 12])
+    rows = rng.choice(M, size=len(SPECIAL_ROWS), replace=False)
+    return {name: int(r) for name, r in zip(SPECIAL_ROWS, rows)}
+
+
+def draw_softmax_logical(M: int, N: int, dist: str, seed: int) -> np.ndarray:
+    """Draw the logical float64 X (M x N) of the recipe above."""
+    rng = np.random.default_rng([seed, 11])
+    X = rng.standard_normal(size=(M, N))
+    if dist == "wide":
+        X *= 30.0
+    elif dist == "specials":
+        if M >= len(SPECIAL_ROWS) and N > 0:
+            sp = softmax_special_rows(M, seed)
+            X[sp["constant"], :] = 0.75
+            cols = rng.choice(N, size=max(1, N // 3), replace=False)
+            X[sp["some_neg_inf"], cols] = -np.inf
+            if N > 1:
+                X[sp["some_neg_inf"], 0] = 0.5      # keep one finite entry
+            X[sp["all_neg_inf"], :] = -np.inf
+            X[sp["pos_inf"], int(rng.integers(N))] = np.inf
+            X[sp["nan"], int(rng.integers(N))] = np.nan
+            X[sp["huge"], :] = np.where(rng.uniform(size=N) < 0.5, -1e4, 1e4)
+    elif dist != "normal":
+        raise ValueError(f"unknown distribution {dist!r}")
+    return X
+
+
+def make_softmax_input(M: int, N: int, dtype, dist: str = "normal", seed: int = 0,
+                       ld_pad: int = 0) -> SoftmaxProblem:
+    """Seeded row-softmax input in the recipe above."""
+    d = dtype_code(dtype)
+    X64 = draw_softmax_logical(M, N, dist, seed)
+    Xr = round_to(X64, d)
+    X, ldx = _store(Xr, False, ld_pad)
+    return SoftmaxProblem(M, N, d, X, ldx, dict(dist=dist, seed=seed, ld_pad=ld_pad))
+
+
+# Row-softmax workloads: the Triton page's example shape and its figure's row count
+# (M = 4096) at the largest row it keeps on chip (about 32K columns).
+SOFTMAX_WORKLOADS = {
+    "softmax_f32_583x931": dict(M=583, N=931, dtype=F32, dist="normal", seed=0),
+    "softmax_f32_4096x32768": dict(M=4096, N=32768, dtype=F32, dist="normal", seed=0),
+    "softmax_f16_4096x32768": dict(M=4096, N=32768, dtype=F16, dist="normal", seed=0),
+}
+
+
 def sweep_ns(start: int = 1536, stop: int = 6144, step: int = 8):
     """N values of the tile/wave-quantization sweep at M=2304, K=4096."""
     return list(range(start, stop + 1, step))
