@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 101
+#define TG_VERSION 102
 
 /* storage type of A, B and C */
 enum tg_dtype { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 };
@@ -199,6 +199,31 @@ int tg_autotune(int64_t M, int64_t N, int64_t K,
                 void *workspace, size_t workspace_bytes,
                 void *stream, int reps,
                 tg_options *best, float *best_us);
+
+/* Row softmax ("OpenAI open-sources Triton", programming-model section: the
+ * fused softmax that normalises each row of X on its own, keeping the row on
+ * chip).  For every row i < M of the row-major M x N matrix X:
+ *
+ *     Y[i][j] = exp(X[i][j] - m_i) / sum_k exp(X[i][k] - m_i),  m_i = max_k X[i][k]
+ *
+ * in float32 arithmetic whatever the storage type (dtype, shared by X and Y),
+ * rounded once (nearest-even) to it.  Rows holding NaN or +inf, or made only
+ * of -inf, give NaN rows; -inf entries of other rows give 0.
+ *
+ * X(i,j) = X[i*ldx + j], Y(i,j) = Y[i*ldy + j]; ldx, ldy >= max(1, N).
+ * Y may be X itself (in place, ldy == ldx); any other overlap is TG_ERR_ARG.
+ * M, N < 2^31; M == 0 or N == 0 does nothing.  Rows up to 32768 elements stay
+ * in registers (one read and one write of X's bytes); longer rows take two
+ * passes (X read twice).  Pointers are caller-owned device memory; work is
+ * enqueued on `stream` and the call returns without waiting.  Returns a
+ * tg_status. */
+int tg_softmax(int64_t M, int64_t N, const void *X, int64_t ldx, void *Y, int64_t ldy, int dtype,
+               void *stream);
+
+/* The launch shape tg_softmax uses for rows of N elements: waves (64 lanes)
+ * per row and 16-byte chunks per lane of the register-resident kernel, or
+ * 0 and 0 for the two-pass long-row kernel.  No device needed. */
+int tg_softmax_shape(int64_t N, int dtype, int32_t *waves_per_row, int32_t *chunks_per_lane);
 
 /* Compute units of the current device, or a negative tg_status. */
 int tg_device_cus(void);

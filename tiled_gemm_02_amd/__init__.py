@@ -88,6 +88,10 @@ def load():
     lib.tg_plan_model.restype = i32
     lib.tg_workspace_size.argtypes = [i64, i64, i64, i32, i32, op]
     lib.tg_workspace_size.restype = ctypes.c_size_t
+    lib.tg_softmax.argtypes = [i64, i64, vp, i64, vp, i64, i32, vp]
+    lib.tg_softmax.restype = i32
+    lib.tg_softmax_shape.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.tg_softmax_shape.restype = i32
     lib.tg_device_cus.argtypes = []
     lib.tg_device_cus.restype = i32
     lib.tg_last_error.argtypes = []
@@ -145,6 +149,11 @@ def _opts(options) -> ctypes.POINTER(Options) | None:
 def tg_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue=None, stream=None) -> int:
     """Raw call: device pointers as integers; returns the status (does not raise)."""
     return load().tg_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, _epi(epilogue), stream)
+
+
+def tg_softmax(M, N, X, ldx, Y, ldy, dtype, stream=None) -> int:
+    """Raw call: device pointers as integers; returns the status (does not raise)."""
+    return load().tg_softmax(M, N, X, ldx, Y, ldy, dtype, stream)
 
 
 def tg_gemm_ex(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue=None, options=None,
@@ -240,6 +249,35 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, o
                            dtype, trans, epi, _opts(options), ws_ptr, ws_bytes, stream)
     _check(rc)
     return out
+
+
+def softmax(X, *, out=None, stream=None):
+    """Row softmax of the 2-D tensor X (tg_softmax): returns Y with Y[i] =
+    softmax(X[i]).  Rows may be strided (X.stride(1) must be 1); ``out`` may be
+    a preallocated tensor of X's shape and dtype, X itself included (in place)."""
+    import torch
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    dtype = _torch_dtype_code(X)
+    M, N = X.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    elif out.shape != X.shape or out.dtype != X.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    if M == 0 or N == 0:
+        return out
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device).cuda_stream
+    _check(load().tg_softmax(M, N, X.data_ptr(), _ld(X), out.data_ptr(), _ld(out), dtype, stream))
+    return out
+
+
+def softmax_shape(N: int, dtype) -> tuple[int, int]:
+    """(waves per row, 16-byte chunks per lane) of tg_softmax for rows of N
+    elements; (0, 0) = the two-pass long-row kernel."""
+    q, c = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().tg_softmax_shape(int(N), int(dtype), ctypes.byref(q), ctypes.byref(c)))
+    return q.value, c.value
 
 
 def autotune(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, out=None,

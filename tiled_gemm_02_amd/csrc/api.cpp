@@ -124,6 +124,16 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_softmax(int dtype, int q, int c, bool vec, const SoftmaxArgs &a, hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F32: return launch_softmax_f32(q, c, vec, a, s);
+    case TG_F16: return launch_softmax_f16(q, c, vec, a, s);
+    case TG_BF16: return launch_softmax_bf16(q, c, vec, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemv(int dtype, bool rows_form, bool vec, int lpr, const GemvArgs &a, hipStream_t s)
 {
     switch (dtype) {
@@ -726,6 +736,68 @@ int tg_device_cus(void)
     if (rc != TG_OK)
         return rc;
     return dev->cus;
+}
+
+int tg_softmax_shape(int64_t N, int dtype, int32_t *waves_per_row, int32_t *chunks_per_lane)
+{
+    if (!waves_per_row || !chunks_per_lane)
+        return fail(TG_ERR_NULL, "output pointer is NULL");
+    if (dtype < TG_F32 || dtype > TG_BF16)
+        return fail(TG_ERR_ARG, "unknown dtype %d", dtype);
+    if (N < 0 || N > INT32_MAX)
+        return fail(TG_ERR_ARG, "N=%lld out of range", (long long)N);
+    int q = 0, c = 0;
+    softmax_shape(dtype, N, &q, &c);
+    *waves_per_row = q;
+    *chunks_per_lane = c;
+    return ok();
+}
+
+int tg_softmax(int64_t M, int64_t N, const void *X, int64_t ldx, void *Y, int64_t ldy, int dtype,
+               void *stream)
+{
+    if (dtype < TG_F32 || dtype > TG_BF16)
+        return fail(TG_ERR_ARG, "unknown dtype %d", dtype);
+    if (M < 0 || N < 0)
+        return fail(TG_ERR_ARG, "negative dimension");
+    if (N > INT32_MAX || M > INT32_MAX)
+        return fail(TG_ERR_ARG, "M and N must be below 2^31");
+    const int64_t need = N > 1 ? N : 1;
+    if (ldx < need || ldy < need)
+        return fail(TG_ERR_ARG, "ldx=%lld / ldy=%lld < max(1, N)=%lld", (long long)ldx,
+                    (long long)ldy, (long long)need);
+    if (M == 0 || N == 0)
+        return ok();
+    if (!X || !Y)
+        return fail(TG_ERR_NULL, "X or Y is NULL");
+    const int64_t span_max = (INT64_MAX / 8 - N) / (M > 1 ? M - 1 : 1);
+    if (ldx > span_max || ldy > span_max)
+        return fail(TG_ERR_ARG, "leading dimension too large for M=%lld", (long long)M);
+    const int64_t es = elem_bytes(dtype);
+    const uintptr_t x0 = (uintptr_t)X, y0 = (uintptr_t)Y;
+    const uintptr_t x1 = x0 + (uintptr_t)(((M - 1) * ldx + N) * es);
+    const uintptr_t y1 = y0 + (uintptr_t)(((M - 1) * ldy + N) * es);
+    if (x0 < y1 && y0 < x1 && !(x0 == y0 && ldx == ldy))
+        return fail(TG_ERR_ARG, "Y overlaps X other than in place (Y == X, ldy == ldx)");
+    DeviceInfo *dev = nullptr;
+    int rc = current_device(&dev);
+    if (rc != TG_OK)
+        return rc;
+    int q = 0, c = 0;
+    softmax_shape(dtype, N, &q, &c);
+    const int E = chunk_elems(dtype);
+    const bool vec = (x0 % 16 == 0) && (y0 % 16 == 0) && (ldx % E == 0) && (ldy % E == 0);
+    SoftmaxArgs a{};
+    a.X = X;
+    a.Y = Y;
+    a.ldx = ldx;
+    a.ldy = ldy;
+    a.M = M;
+    a.N = (int)N;
+    const hipError_t e = launch_softmax(dtype, q, c, vec, a, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(TG_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 const char *tg_last_error(void) { return g_err.c_str(); }

@@ -8,6 +8,7 @@
 #include "gemv.hpp"
 #include "mfma_gemm.hpp"
 #include "skinny.hpp"
+#include "softmax.hpp"
 
 namespace tg {
 
@@ -35,6 +36,9 @@ hipError_t launch_scale_c(int dtype, void *C, int M, int N, int64_t ldc, const O
 hipError_t launch_gemv(int dtype, bool rows_form, bool vec, int lpr, const GemvArgs &a,
                        hipStream_t s);
 hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream_t s);
+// Row softmax: q waves per row and c 16-byte chunks per lane (row kept in
+// registers), or q == 0 for the two-pass long-row kernel.
+hipError_t launch_softmax(int dtype, int q, int c, bool vec, const SoftmaxArgs &a, hipStream_t s);
 
 #define TG_DECLARE_TYPE_LAUNCHERS(NAME)                                                          \
     hipError_t launch_mfma_##NAME(int trans, int bm, int bn, bool vec, const MfmaArgs &a,        \
@@ -51,7 +55,8 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
                                   hipStream_t s);                                                \
     hipError_t launch_skinny_##NAME(bool trans_b, const SkinnyArgs &a, hipStream_t s);           \
     hipError_t launch_mfma2_##NAME(int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s); \
-    int mfma2_occupancy_##NAME(int trans, int bm, int bn);
+    int mfma2_occupancy_##NAME(int trans, int bm, int bn);                                       \
+    hipError_t launch_softmax_##NAME(int q, int c, bool vec, const SoftmaxArgs &a, hipStream_t s);
 
 TG_DECLARE_TYPE_LAUNCHERS(f16)
 TG_DECLARE_TYPE_LAUNCHERS(bf16)

@@ -400,6 +400,32 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
 
 // ---------------------------------------------------------------- entry
 
+// ---------------------------------------------------------------- row softmax
+
+void softmax_shape(int dtype, int64_t N, int *q, int *c)
+{
+    // capacities 256 .. 32768 elements; one wave per row up to 1 KiB-4 KiB rows,
+    // then more waves per row before more chunks per lane (more loads in flight
+    // per row, the same registers per lane).  32 values per lane at most: a
+    // 1024-thread workgroup has 128 registers per lane, and 64 values spill.
+    static const int f32_shapes[][2] = {{1, 1}, {1, 2}, {1, 4}, {2, 4}, {4, 4},
+                                        {8, 4}, {16, 4}, {16, 8}};
+    static const int h16_shapes[][2] = {{1, 1}, {1, 2}, {2, 2}, {4, 2},
+                                        {8, 2}, {16, 2}, {16, 4}};
+    const int E = chunk_elems(dtype);
+    const int (*shapes)[2] = E == 4 ? f32_shapes : h16_shapes;
+    const int n = E == 4 ? 8 : 7;
+    for (int i = 0; i < n; ++i) {
+        if ((int64_t)shapes[i][0] * 64 * shapes[i][1] * E >= N) {
+            *q = shapes[i][0];
+            *c = shapes[i][1];
+            return;
+        }
+    }
+    *q = 0;
+    *c = 0;
+}
+
 // ---------------------------------------------------------------- aligned copies
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }

@@ -89,4 +89,11 @@ Problem packed_problem(const Problem &p);
 inline int chunk_elems(int dtype) { return dtype == TG_F32 ? 4 : 8; }
 inline int elem_bytes(int dtype) { return dtype == TG_F32 ? 4 : 2; }
 
+// Row softmax launch shape for rows of N elements: the smallest register-
+// resident form (q wave64s per row, c 16-byte chunks per lane, capacity
+// q * 64 * c * chunk_elems) that holds the row, or q = c = 0 for the two-pass
+// long-row kernel (N above kSoftmaxMaxResident).
+constexpr int64_t kSoftmaxMaxResident = 32768;
+void softmax_shape(int dtype, int64_t N, int *q, int *c);
+
 }  // namespace tg
