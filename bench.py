@@ -34,23 +34,34 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["tiled_gemm_02_amd/csrc/kernels/common.hpp",
-                  "tiled_gemm_02_amd/csrc/kernels/mfma_gemm.hpp",
-                  "tiled_gemm_02_amd/csrc/kernels/mfma_gemm3.hpp",
-                  "tiled_gemm_02_amd/csrc/kernels/mfma_pingpong.hpp",
-                  "tiled_gemm_02_amd/csrc/kernels/instances.inc",
-                  "tiled_gemm_02_amd/csrc/kernels/gemv.hpp",
-                  "tiled_gemm_02_amd/csrc/kernels/skinny.hpp",
-                  "tiled_gemm_02_amd/csrc/kernels/aux_kernels.hpp"]
+_K = "tiled_gemm_02_amd/csrc/kernels/"
+# The sources each kernel family's code comes from: its counters are void once
+# any of them changes.
+KERNEL_SOURCES = {
+    "mfma": [_K + "common.hpp", _K + "mfma_gemm.hpp", _K + "mfma_gemm3.hpp", _K + "mfma_pingpong.hpp"],
+    "skinny": [_K + "common.hpp", _K + "skinny.hpp"],
+    "gemv": [_K + "common.hpp", _K + "gemv.hpp"],
+    "softmax": [_K + "common.hpp", _K + "softmax.hpp"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_family(workload: str) -> str:
+    if workload.startswith("softmax_"):
+        return "softmax"
+    if "skinny" in workload:
+        return "skinny"
+    if "gemv" in workload:
+        return "gemv"
+    return "mfma"
+
+
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[family]:
         path = os.path.join(ROOT, rel)
         if os.path.exists(path):
             h.update(open(path, "rb").read())
@@ -64,7 +75,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     ent = data.get(workload)
-    if not ent or ent.get("kernel_hash") != kernel_source_hash():
+    if not ent or ent.get("kernel_hash") != kernel_source_hash(kernel_family(workload)):
         return None
     return ent.get("bytes_per_launch")
 
@@ -148,6 +159,47 @@ def time_workload(name: str, steps: int, warmup: int, device, rotate: bool):
                 plan=plan)
 
 
+def prepare_softmax(name: str, device):
+    import torch
+    from gemm_inputs import DTYPE_NAMES, ELEM_BYTES, SOFTMAX_WORKLOADS, make_softmax_input
+    w = SOFTMAX_WORKLOADS[name]
+    p = make_softmax_input(w["M"], w["N"], w["dtype"], w["dist"], w["seed"])
+    X = dev_tensor(p.X, p.dtype, device)
+    s = ELEM_BYTES[p.dtype]
+    copies = max(1, math.ceil(ROTATE_BYTES / (s * p.M * p.N)))
+    Xs = [X] + [X.clone() for _ in range(copies - 1)]
+    Y = torch.empty_like(X)
+    return dict(p=p, Xs=Xs, Y=Y, copies=copies, alg_bytes=2 * s * p.M * p.N,
+                dtype=DTYPE_NAMES[p.dtype])
+
+
+def time_softmax(name: str, steps: int, warmup: int, device):
+    """One step = tg_softmax over the whole M x N input (rotated over copies
+    whose total passes the last-level cache), timed with HIP events on the
+    launch stream."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    d = prepare_softmax(name, device)
+    p = d["p"]
+    stream = torch.cuda.current_stream(device)
+
+    def step(i):
+        tg.softmax(d["Xs"][i % d["copies"]], out=d["Y"], stream=stream.cuda_stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize(device)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize(device)
+    total_ms = evs[0].elapsed_time(evs[-1])
+    q, c = tg.softmax_shape(p.N, p.dtype)
+    return dict(name=name, p=p, d=d, ms_per_step=total_ms / steps, shape=(q, c))
+
+
 def cpu_baseline(name: str, target_s: float):
     """The oracle on a bounded sample of output rows of the workload, on the host cores."""
     import numpy as np
@@ -205,9 +257,11 @@ def roofline_entry(r, bound):
 # files into TRAFFIC_FILE, tagged with a hash of the kernel sources so that a
 # changed kernel reports null until it is measured again.
 
-TRAFFIC_WORKLOADS = ["f16_8192", "f16_skinny_8192x128x8192", "f16_gemv_1x8192x8192"]
+TRAFFIC_WORKLOADS = ["f16_8192", "f16_skinny_8192x128x8192", "f16_gemv_1x8192x8192",
+                     "softmax_f32_4096x32768", "softmax_f16_4096x32768"]
 COPY_BYTES = 256 << 20
-DOMINANT = {"mfma": "mfma_", "skinny": "skinny_kernel"}   # GEMV: gemv_cols / gemv_rows
+DOMINANT = {"mfma": "mfma_", "skinny": "skinny_kernel", "softmax": "softmax_rows_kernel"}
+# GEMV: gemv_cols / gemv_rows
 
 
 def traffic_kernel(name: str, launches: int = 6):
@@ -221,11 +275,12 @@ def traffic_kernel(name: str, launches: int = 6):
             dst.copy_(src)
         torch.cuda.synchronize(device)
         return
-    import tiled_gemm_02_amd as tg
+    if name.startswith("softmax_"):
+        time_softmax(name, launches, 1, device)
+        return
     from gemm_inputs import WORKLOADS
     w = WORKLOADS[name]
     time_workload(name, launches, 1, device, rotate=w["N"] <= 256 or w["M"] == 1)
-    del tg
 
 
 def _counter_avg(csv_path: str, sub: str, counter: str):
@@ -242,7 +297,7 @@ def _counter_avg(csv_path: str, sub: str, counter: str):
 def traffic_summarize(root: str):
     import glob
     import tiled_gemm_02_amd as tg
-    from gemm_inputs import ELEM_BYTES, WORKLOADS
+    from gemm_inputs import ELEM_BYTES, SOFTMAX_WORKLOADS, WORKLOADS
 
     def find(tag):
         f = glob.glob(os.path.join(root, tag, "**", "*counter_collection.csv"), recursive=True)
@@ -269,24 +324,30 @@ def traffic_summarize(root: str):
              "| Workload | Kernel | Fetch (MiB) | Write (MiB) | Total (MiB) | Algorithmic (MiB) | Ratio |",
              "|---|---|---|---|---|---|---|"]
     for name in TRAFFIC_WORKLOADS:
-        w = WORKLOADS[name]
-        plan = tg.tg_plan_model(w["M"], w["N"], w["K"], w["dtype"], w["trans"], num_cus=256)
-        if plan["path_name"] == "gemv":
-            sub = "gemv_rows" if plan["tile_m"] == 4 else "gemv_cols"
+        fam = kernel_family(name)
+        if fam == "softmax":
+            w = SOFTMAX_WORKLOADS[name]
+            sub = DOMINANT["softmax"] if w["N"] <= 32768 else "softmax_long_kernel"
+            alg = 2 * ELEM_BYTES[w["dtype"]] * w["M"] * w["N"]
         else:
-            sub = DOMINANT[plan["path_name"]]
+            w = WORKLOADS[name]
+            plan = tg.tg_plan_model(w["M"], w["N"], w["K"], w["dtype"], w["trans"], num_cus=256)
+            if plan["path_name"] == "gemv":
+                sub = "gemv_rows" if plan["tile_m"] == 4 else "gemv_cols"
+            else:
+                sub = DOMINANT[plan["path_name"]]
+            alg = ELEM_BYTES[w["dtype"]] * (w["M"] * w["K"] + w["K"] * w["N"] + w["M"] * w["N"])
         f, nf = _counter_avg(find(name + "_fetch"), sub, "FETCH_SIZE")
         wr, nw = _counter_avg(find(name + "_write"), sub, "WRITE_SIZE")
         if f is None or wr is None:
             raise SystemExit(f"no {sub} dispatches for {name}")
         fb, wb = f * 1024.0 * k_fetch, wr * 1024.0 * k_write
-        alg = ELEM_BYTES[w["dtype"]] * (w["M"] * w["K"] + w["K"] * w["N"] + w["M"] * w["N"])
-        out[name] = {"kernel": sub, "kernel_hash": kernel_source_hash(), "fetch_bytes": fb,
+        out[name] = {"kernel": sub, "kernel_hash": kernel_source_hash(fam), "fetch_bytes": fb,
                      "write_bytes": wb, "bytes_per_launch": fb + wb, "alg_bytes": alg,
                      "dispatches": [nf, nw]}
         lines.append(f"| {name} | `{sub}` | {fb / 2**20:.1f} | {wb / 2**20:.1f} | {(fb + wb) / 2**20:.1f} | "
                      f"{alg / 2**20:.1f} | {(fb + wb) / alg:.3f} |")
-    lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", ""]
+    lines += ["", "Kernel source hashes: " + ", ".join(f"{f} `{kernel_source_hash(f)}`" for f in KERNEL_SOURCES), ""]
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
     open(os.path.join(ROOT, "profiles", "traffic_summary.md"), "w").write("\n".join(lines))
     print("\n".join(lines))
@@ -439,13 +500,73 @@ def align_sweep(out_path: str, reps: int = 5):
     print("\n".join(lines))
 
 
+def softmax_sweep(out_path: str, reps: int = 20):
+    """Row softmax at M = 4096 over row lengths N = 256 .. 32768 and beyond (the
+    shape of the Triton page's A100 figure, "OpenAI open-sources Triton",
+    programming-model section), float32 and float16, in GB/s of one read and
+    one write of X.  torch.softmax on the same tensors is timed beside it as
+    context.  Inputs N(0, 1) from a seeded device generator; each point is the
+    median of `reps` timed calls after two warm-up calls, alternating between
+    enough input copies to exceed the last-level cache."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    device = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(device)
+    g = torch.Generator(device=device).manual_seed(8)
+    M = 4096
+    lines = ["# Row softmax sweep, M = 4096", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"python3 bench.py --softmax-sweep {out_path}", "```", "",
+             "GB/s = 2 M N (element bytes) / time: one read of X and one write of Y. Shape = waves",
+             "per row x 16-byte chunks per lane of the register-resident kernel (0x0: two-pass",
+             "kernel, which reads X twice). torch.softmax(dim=1) on the same tensors and a plain",
+             "device copy of X into Y (the same bytes moved, no arithmetic) are context.", "",
+             "| dtype | N | shape | us | GB/s | % of 8 TB/s | torch us | torch GB/s | copy GB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+
+    def timed(fn, xs):
+        for i in range(2):
+            fn(xs[i % len(xs)])
+        ts = []
+        for i in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(xs[i % len(xs)])
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    for dt, tdt in [("f32", torch.float32), ("f16", torch.float16)]:
+        for N in [256, 512, 1024, 2048, 4096, 8192, 12288, 16384, 24576, 32768, 65536]:
+            es = torch.tensor([], dtype=tdt).element_size()
+            copies = max(2, math.ceil(ROTATE_BYTES / (M * N * es)))
+            xs = [torch.randn((M, N), generator=g, device=device).to(tdt) for _ in range(copies)]
+            Y = torch.empty_like(xs[0])
+            ms = timed(lambda x: tg.softmax(x, out=Y, stream=stream.cuda_stream), xs)
+            mt = timed(lambda x: torch.softmax(x, dim=1), xs)
+            mc = timed(lambda x: Y.copy_(x), xs)
+            gbs, gbt = 2 * M * N * es / ms / 1e6, 2 * M * N * es / mt / 1e6
+            gbc = 2 * M * N * es / mc / 1e6
+            q, c = tg.softmax_shape(N, tg.TG_F32 if dt == "f32" else tg.TG_F16)
+            lines.append(f"| {dt} | {N} | {q}x{c} | {ms * 1e3:.1f} | {gbs:.0f} | {gbs / PEAK_HBM_GBS * 100:.1f} | "
+                         f"{mt * 1e3:.1f} | {gbt:.0f} | {gbc:.0f} |")
+            log(lines[-1])
+            del xs, Y
+            torch.cuda.empty_cache()
+    lines.append("")
+    open(out_path, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="f16_8192")
-    ap.add_argument("--secondary", default="f16_skinny_8192x128x8192,f16_gemv_1x8192x8192",
+    ap.add_argument("--secondary", default="f16_skinny_8192x128x8192,f16_gemv_1x8192x8192,"
+                    "softmax_f32_4096x32768,softmax_f16_4096x32768",
                     help="comma-separated memory-bound workloads reported alongside ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -456,6 +577,8 @@ def main():
                     help="with --sweep: also time tg_autotune's best plan at every point")
     ap.add_argument("--align-sweep", default=None,
                     help="run the K-alignment sweep, write its summary to this file, then exit")
+    ap.add_argument("--softmax-sweep", default=None,
+                    help="run the M=4096 row-softmax sweep over N, write its summary to this file, then exit")
     ap.add_argument("--traffic-kernel", default=None,
                     help="run one workload (or 'copy') for a rocprofv3 counter pass, then exit")
     ap.add_argument("--traffic-summarize", default=None,
@@ -487,6 +610,9 @@ def main():
         return
     if args.align_sweep:
         align_sweep(args.align_sweep)
+        return
+    if args.softmax_sweep:
+        softmax_sweep(args.softmax_sweep)
         return
     log("device", torch.cuda.get_device_name(0), "cus", tg.tg_device_cus())
 
@@ -525,6 +651,18 @@ def main():
     sec = []
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
         log("timing", name)
+        if name.startswith("softmax_"):
+            rs = time_softmax(name, max(args.steps, 50), args.warmup, device)
+            ent = roofline_entry(rs, "hbm")
+            p = rs["p"]
+            sec.append({"workload": name, "value": ent["achieved"], "unit": "GB/s",
+                        "ms_per_step": round(rs["ms_per_step"], 5),
+                        "config": {"M": p.M, "N": p.N, "dtype": rs["d"]["dtype"],
+                                   "waves_per_row": rs["shape"][0], "chunks_per_lane": rs["shape"][1]},
+                        "roofline": ent, "rotated_copies": rs["d"]["copies"]})
+            del rs
+            torch.cuda.empty_cache()
+            continue
         rs = time_workload(name, max(args.steps, 50), args.warmup, device, rotate=True)
         ent = roofline_entry(rs, "hbm")
         sec.append({"workload": name, "value": ent["achieved"], "unit": "GB/s",

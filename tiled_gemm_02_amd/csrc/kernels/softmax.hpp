@@ -16,6 +16,9 @@
 // butterfly reductions across the wave (__shfl_xor) and, for Q > 1, across
 // its waves through LDS, and exp(x - m) is evaluated as 2^((x - m) log2 e).
 // Each lane sums its own C E <= 32 values in sequence before the tree.
+// 16-bit rows stay packed in registers and their exponentials are computed
+// twice (for the sum and for the output), which halves the registers a row
+// needs; the recomputed values are bit-identical to the first ones.
 //
 // Long rows (N > 32768): one 1024-thread workgroup per row makes two passes.
 // The first keeps, per thread, a running maximum and a sum of exponentials
@@ -62,15 +65,38 @@ __device__ __forceinline__ float sm_wave_sum(float x)
     return x;
 }
 
+// Cache policy of the 16-byte row accesses (a bit set: non-temporal, i.e.
+// streamed past the caches).  Chosen per launch shape from measurements.
+enum : int { kSmNtStore = 1, kSmNtLoad = 2 };
+
+template <int CP>
+__device__ __forceinline__ u32x4 sm_ld16(const void *p)
+{
+    if constexpr ((CP & kSmNtLoad) != 0)
+        return __builtin_nontemporal_load((const u32x4 *)p);
+    else
+        return *(const u32x4 *)p;
+}
+
+template <int CP>
+__device__ __forceinline__ void sm_st16(void *p, const u32x4 &c)
+{
+    if constexpr ((CP & kSmNtStore) != 0)
+        __builtin_nontemporal_store(c, (u32x4 *)p);
+    else
+        *(u32x4 *)p = c;
+}
+
 // E consecutive elements starting at j0 of a row, as float32; elements at or
-// past N read as -inf.  VEC: the row start is 16-byte aligned.
-template <typename Tr, bool VEC>
-__device__ __forceinline__ void sm_load(const typename Tr::T *row, int64_t j0, int64_t N,
+// past N read as -inf.  VEC: the row start is 16-byte aligned.  (Indices are
+// 32-bit: a row segment holds fewer than 2^31 elements.)
+template <typename Tr, bool VEC, int CP = 0>
+__device__ __forceinline__ void sm_load(const typename Tr::T *row, int j0, int N,
                                         float (&v)[Tr::E])
 {
     constexpr int E = Tr::E;
     if (VEC && j0 + E <= N) {
-        const u32x4 c = *(const u32x4 *)(row + j0);
+        const u32x4 c = sm_ld16<CP>(row + j0);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const uint32_t bits = chunk_elem<Tr::kBytes>(c, e);
@@ -86,8 +112,8 @@ __device__ __forceinline__ void sm_load(const typename Tr::T *row, int64_t j0, i
     }
 }
 
-template <typename Tr, bool VEC>
-__device__ __forceinline__ void sm_store(typename Tr::T *row, int64_t j0, int64_t N,
+template <typename Tr, bool VEC, int CP = 0>
+__device__ __forceinline__ void sm_store(typename Tr::T *row, int j0, int N,
                                          const float (&v)[Tr::E])
 {
     constexpr int E = Tr::E;
@@ -106,7 +132,7 @@ __device__ __forceinline__ void sm_store(typename Tr::T *row, int64_t j0, int64_
                 c[w] = lo | (hi << 16);
             }
         }
-        *(u32x4 *)(row + j0) = c;
+        sm_st16<CP>(row + j0, c);
     } else {
 #pragma unroll
         for (int e = 0; e < E; ++e)
@@ -118,12 +144,49 @@ __device__ __forceinline__ void sm_store(typename Tr::T *row, int64_t j0, int64_
 template <int Q>
 constexpr int sm_rows_per_block() { return Q >= 4 ? 1 : 4 / Q; }
 
-template <typename Tr, int Q, int C, bool VEC>
-__global__ __launch_bounds__(64 * Q * sm_rows_per_block<Q>()) void softmax_rows_kernel(SoftmaxArgs p)
+// One 16-byte chunk of a 16-bit row as raw bits (8 elements), elements at or
+// past N filled with -inf.  Rows of 16-bit values stay in registers in this
+// packed form (half the registers of float32 copies): every pass converts
+// them again, and the exponentials are recomputed for the output.
+template <typename Tr, bool VEC, int CP>
+__device__ __forceinline__ u32x4 sm_load_raw16(const typename Tr::T *row, int j0, int N)
+{
+    static_assert(Tr::kBytes == 2, "16-bit storage");
+    if (VEC && j0 + 8 <= N)
+        return sm_ld16<CP>(row + j0);
+    const uint32_t ninf = __builtin_bit_cast(uint16_t, Tr::from_f32(-INFINITY));
+    const uint16_t *r16 = (const uint16_t *)row;
+    u32x4 c;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = (j0 + 2 * w < N) ? r16[j0 + 2 * w] : ninf;
+        const uint32_t hi = (j0 + 2 * w + 1 < N) ? r16[j0 + 2 * w + 1] : ninf;
+        c[w] = lo | (hi << 16);
+    }
+    return c;
+}
+
+template <typename Tr>
+__device__ __forceinline__ float sm_raw16_f32(const u32x4 &c, int e)
+{
+    return Tr::to_f32(__builtin_bit_cast(typename Tr::T, (uint16_t)chunk_elem<2>(c, e)));
+}
+
+// Sixteen-wave rows ask for two resident workgroups per CU (64 registers per
+// lane), so that one row's loads overlap the other's reductions and stores
+// (the element-wise form, for unaligned rows, would spill at 64).
+template <int Q, bool VEC>
+constexpr int sm_waves_per_eu() { return Q == 16 && VEC ? 8 : 1; }
+
+// CP: cache policy of the row's 16-byte loads and stores (kSmNt* bits).
+template <typename Tr, int Q, int C, bool VEC, int CP>
+__global__ __launch_bounds__(64 * Q * sm_rows_per_block<Q>())
+__attribute__((amdgpu_waves_per_eu(sm_waves_per_eu<Q, VEC>()))) void softmax_rows_kernel(SoftmaxArgs p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = typename Tr::T;
     constexpr int E = Tr::E;
+    constexpr bool RAW = Tr::kBytes == 2;
     constexpr int RPB = sm_rows_per_block<Q>();
     static_assert(C * E <= 32, "at most 32 values per lane (registers; sequential part of the sum)");
     __shared__ float red[2][RPB][Q];
@@ -135,19 +198,32 @@ __global__ __launch_bounds__(64 * Q * sm_rows_per_block<Q>()) void softmax_rows_
     const bool active = r < p.M;   // every wave still takes part in the barriers
     const T *x = (const T *)p.X + (active ? r : 0) * p.ldx;
     T *y = (T *)p.Y + (active ? r : 0) * p.ldy;
-    const int64_t N = active ? p.N : 0;
+    const int N = active ? p.N : 0;
 
-    float v[C][E];
+    // the row: float32 values, or packed 16-bit chunks
+    float v[RAW ? 1 : C][E];
+    u32x4 raw[RAW ? C : 1];
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-        sm_load<Tr, VEC>(x, (int64_t)((c * Q + qw) * 64 + lane) * E, N, v[c]);
+    for (int c = 0; c < C; ++c) {
+        const int j0 = ((c * Q + qw) * 64 + lane) * E;
+        if constexpr (RAW)
+            raw[c] = sm_load_raw16<Tr, VEC, CP>(x, j0, N);
+        else
+            sm_load<Tr, VEC, CP>(x, j0, N, v[c]);
+    }
+    auto val = [&](int c, int e) -> float {
+        if constexpr (RAW)
+            return sm_raw16_f32<Tr>(raw[c], e);
+        else
+            return v[c][e];
+    };
 
     float mx = -INFINITY;
 #pragma unroll
     for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            mx = fmaxf(mx, v[c][e]);
+            mx = fmaxf(mx, val(c, e));
     mx = sm_wave_max(mx);
     if constexpr (Q > 1) {
         if (lane == 0)
@@ -164,8 +240,10 @@ __global__ __launch_bounds__(64 * Q * sm_rows_per_block<Q>()) void softmax_rows_
     for (int c = 0; c < C; ++c)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            v[c][e] = exp2f((v[c][e] - mx) * kLog2e);
-            s += v[c][e];
+            const float ex = exp2f((val(c, e) - mx) * kLog2e);
+            if constexpr (!RAW)
+                v[c][e] = ex;
+            s += ex;
         }
     s = sm_wave_sum(s);
     if constexpr (Q > 1) {
@@ -189,10 +267,15 @@ __global__ __launch_bounds__(64 * Q * sm_rows_per_block<Q>()) void softmax_rows_
     if (active) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
+            float o[E];
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                v[c][e] *= inv;
-            sm_store<Tr, VEC>(y, (int64_t)((c * Q + qw) * 64 + lane) * E, N, v[c]);
+            for (int e = 0; e < E; ++e) {
+                if constexpr (RAW)
+                    o[e] = exp2f((val(c, e) - mx) * kLog2e) * inv;
+                else
+                    o[e] = v[c][e] * inv;
+            }
+            sm_store<Tr, VEC, CP>(y, ((c * Q + qw) * 64 + lane) * E, N, o);
         }
     }
 #endif
@@ -250,10 +333,11 @@ __global__ __launch_bounds__(kSoftmaxLongThreads) void softmax_long_kernel(Softm
 
     float m = -INFINITY, s = 0.0f;
     for (int64_t base = 0; base < N; base += STEP) {
+        const int rem = (int)min<int64_t>(N - base, STEP);
         float v[U][E];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            sm_load<Tr, VEC>(x, base + (int64_t)(u * kSoftmaxLongThreads + tid) * E, N, v[u]);
+            sm_load<Tr, VEC>(x + base, (u * kSoftmaxLongThreads + tid) * E, rem, v[u]);
         float cm = -INFINITY;
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -276,16 +360,17 @@ __global__ __launch_bounds__(kSoftmaxLongThreads) void softmax_long_kernel(Softm
     const float inv = 1.0f / S;
 
     for (int64_t base = 0; base < N; base += STEP) {
+        const int rem = (int)min<int64_t>(N - base, STEP);
         float v[U][E];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            sm_load<Tr, VEC>(x, base + (int64_t)(u * kSoftmaxLongThreads + tid) * E, N, v[u]);
+            sm_load<Tr, VEC>(x + base, (u * kSoftmaxLongThreads + tid) * E, rem, v[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 v[u][e] = exp2f((v[u][e] - m) * kLog2e) * inv;
-            sm_store<Tr, VEC>(y, base + (int64_t)(u * kSoftmaxLongThreads + tid) * E, N, v[u]);
+            sm_store<Tr, VEC>(y + base, (u * kSoftmaxLongThreads + tid) * E, rem, v[u]);
         }
     }
 #endif
