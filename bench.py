@@ -371,6 +371,7 @@ def sweep(out_path: str, step: int, reps: int = 5, tune: bool = False):
     Cfull = torch.empty((M, 6144), dtype=torch.float16, device=device)
     stream = torch.cuda.current_stream(device)
     fixed = dict(path=tg.TG_PATH_MFMA, tile_m=256, tile_n=256, split_k=1)
+    tg.tune_cache_clear()   # the planner column is the heuristic, not a recorded winner
 
     # split-K partials go to one persistent workspace (as in the timed bench)
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=device)

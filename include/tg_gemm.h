@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 102
+#define TG_VERSION 103
 
 /* storage type of A, B and C */
 enum tg_dtype { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 };
@@ -189,7 +189,16 @@ size_t tg_workspace_size(int64_t M, int64_t N, int64_t K, int dtype, int trans,
  * slope; its alpha and beta are not applied while timing (beta would feed
  * each run's C into the next).  Blocks until the timing is done.  workspace
  * as for tg_gemm_ex (NULL: allocations are made per run).  Plans that need
- * more workspace than given are skipped.  Returns a tg_status. */
+ * more workspace than given are skipped.  Returns a tg_status.
+ *
+ * The winner is also recorded in a cache the library keeps per device, keyed
+ * by the problem as the planner sees it (M, N, K, dtype, trans, lda, ldb, ldc
+ * and whether A and B are 16-byte aligned; not the epilogue).  Later calls of
+ * tg_gemm, tg_gemm_ex with opts == NULL, and tg_gemm_plan with opts == NULL
+ * (which assumes packed, aligned operands) on the same device and problem use
+ * the recorded plan instead of the heuristic; when a recorded K split finds
+ * no room for its workspace, the call falls back as an unforced plan does.
+ * The cache lives until the process ends or tg_tune_cache_clear. */
 int tg_autotune(int64_t M, int64_t N, int64_t K,
                 const void *A, int64_t lda,
                 const void *B, int64_t ldb,
@@ -224,6 +233,14 @@ int tg_softmax(int64_t M, int64_t N, const void *X, int64_t ldx, void *Y, int64_
  * per row and 16-byte chunks per lane of the register-resident kernel, or
  * 0 and 0 for the two-pass long-row kernel.  No device needed. */
 int tg_softmax_shape(int64_t N, int dtype, int32_t *waves_per_row, int32_t *chunks_per_lane);
+
+/* Forget every plan tg_autotune recorded on the current device.  Returns a
+ * tg_status. */
+int tg_tune_cache_clear(void);
+
+/* Number of plans tg_autotune has recorded on the current device, or a
+ * negative tg_status. */
+int64_t tg_tune_cache_size(void);
 
 /* Compute units of the current device, or a negative tg_status. */
 int tg_device_cus(void);

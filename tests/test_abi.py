@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert tg.tg_version() == 102
+    assert tg.tg_version() == 103
 
 
 def test_epilogue_struct_matches_header(tmp_path):
@@ -91,6 +91,8 @@ def test_no_device_is_reported():
     rc = tg.tg_gemm(4, 4, 4, 1, 4, 1, 4, 1, 4, tg.TG_F16, 0)
     assert rc == tg.TG_ERR_DEVICE
     assert tg.tg_device_cus() == tg.TG_ERR_DEVICE
+    assert tg.load().tg_tune_cache_size() == tg.TG_ERR_DEVICE
+    assert tg.load().tg_tune_cache_clear() == tg.TG_ERR_DEVICE
     with pytest.raises(tg.TgError):
         tg.tg_gemm_plan(64, 64, 64, tg.TG_F16)
 

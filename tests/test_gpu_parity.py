@@ -406,6 +406,47 @@ def test_autotune_choice_is_valid_and_correct(shape):
     assert opts["path"] in (tg.TG_PATH_AUTO, tg.TG_PATH_MFMA, tg.TG_PATH_SKINNY)
     r, _, _ = check_full(p, options=None if opts["path"] == tg.TG_PATH_AUTO else opts, workspace=ws)
     assert r["ok"], (opts, r)
+    tg.tune_cache_clear()
+
+
+def test_autotune_winner_is_cached_and_used():
+    """tg_autotune records its winner per problem; calls without options then
+    plan with it (tg_gemm_plan shows the same tile and split), still match the
+    oracle, and run with too small a workspace; clearing the cache restores
+    the heuristic."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    M, N, K = 1536, 2048, 4096
+    _say("case autotune cache", (M, N, K))
+    tg.tune_cache_clear()
+    assert tg.tune_cache_size() == 0
+    p = make_problem(M, N, K, F16, NN, "normal", seed=43)
+    A = to_device(p.A, p.dtype)
+    B = to_device(p.B, p.dtype)
+    heuristic = tg.plan_for(A, B)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda:0")
+    opts, _ = tg.autotune(A, B, workspace=ws, reps=2)
+    assert tg.tune_cache_size() == 1
+    want = heuristic if opts["path"] == tg.TG_PATH_AUTO else tg.plan_for(A, B, options=opts)
+    got = tg.plan_for(A, B)
+    for k in ("path", "tile_m", "tile_n", "split_k"):
+        assert got[k] == want[k], (k, got, want, opts)
+    # the cached plan runs without options, with or without room for a split
+    r, _, _ = check_full(p)
+    assert r["ok"], r
+    small = torch.empty(4096, dtype=torch.uint8, device="cuda:0")
+    r, _, _ = check_full(p, workspace=small)
+    assert r["ok"], r
+    # the same sizes with another leading dimension are another problem
+    p2 = make_problem(M, N, K, F16, NN, "normal", seed=44, ld_pad=8)
+    r, _, _ = check_full(p2)
+    assert r["ok"], r
+    assert tg.tune_cache_size() == 1
+    tg.tune_cache_clear()
+    assert tg.tune_cache_size() == 0
+    again = tg.plan_for(A, B)
+    for k in ("path", "tile_m", "tile_n", "split_k"):
+        assert again[k] == heuristic[k]
 
 
 # ---------------------------------------------------------------- aligned copies

@@ -92,6 +92,10 @@ def load():
     lib.tg_softmax.restype = i32
     lib.tg_softmax_shape.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.tg_softmax_shape.restype = i32
+    lib.tg_tune_cache_clear.argtypes = []
+    lib.tg_tune_cache_clear.restype = i32
+    lib.tg_tune_cache_size.argtypes = []
+    lib.tg_tune_cache_size.restype = i64
     lib.tg_device_cus.argtypes = []
     lib.tg_device_cus.restype = i32
     lib.tg_last_error.argtypes = []
@@ -270,6 +274,19 @@ def softmax(X, *, out=None, stream=None):
         stream = torch.cuda.current_stream(X.device).cuda_stream
     _check(load().tg_softmax(M, N, X.data_ptr(), _ld(X), out.data_ptr(), _ld(out), dtype, stream))
     return out
+
+
+def tune_cache_clear() -> None:
+    """Forget the plans tg_autotune recorded on the current device."""
+    _check(load().tg_tune_cache_clear())
+
+
+def tune_cache_size() -> int:
+    """Plans tg_autotune has recorded on the current device."""
+    n = int(load().tg_tune_cache_size())
+    if n < 0:
+        _check(n)
+    return n
 
 
 def softmax_shape(N: int, dtype) -> tuple[int, int]:

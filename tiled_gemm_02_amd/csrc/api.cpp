@@ -6,7 +6,9 @@
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <tuple>
 #include <string>
 #include <vector>
 
@@ -167,6 +169,24 @@ static int ok()
 
 // ---------------------------------------------------------------- device facts
 
+// A problem as the planner sees it: sizes, layout, leading dimensions and
+// alignment (the epilogue does not change the plan).
+struct TuneKey {
+    int64_t M, N, K, lda, ldb, ldc;
+    int dtype, trans;
+    bool aligned;
+    bool operator<(const TuneKey &o) const
+    {
+        return std::tie(M, N, K, lda, ldb, ldc, dtype, trans, aligned) <
+               std::tie(o.M, o.N, o.K, o.lda, o.ldb, o.ldc, o.dtype, o.trans, o.aligned);
+    }
+};
+
+static TuneKey tune_key(const Problem &p)
+{
+    return TuneKey{p.M, p.N, p.K, p.lda, p.ldb, p.ldc, p.dtype, p.trans, p.ptrs_aligned};
+}
+
 struct DeviceInfo {
     bool probed = false;
     bool gfx950 = false;
@@ -180,7 +200,23 @@ struct DeviceInfo {
     bool pool_tried = false;
     // measured residency per (dtype, trans, tile, vec), 0 = not yet asked
     int occ[3][4][8][2] = {};
+    // benchmark-mode winners (tg_autotune) per problem, used by calls that
+    // pass no options; guarded by g_tune_mu
+    std::map<TuneKey, tg_options> tuned;
 };
+
+static std::mutex g_tune_mu;
+
+// The cached benchmark-mode winner for p, if there is one.
+static bool tune_lookup(DeviceInfo *dev, const Problem &p, tg_options *out)
+{
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    auto it = dev->tuned.find(tune_key(p));
+    if (it == dev->tuned.end())
+        return false;
+    *out = it->second;
+    return true;
+}
 
 static std::mutex g_dev_mu;
 static DeviceInfo g_dev[64];
@@ -492,9 +528,20 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
     Chip chip = device_chip(*dev);
     tg_plan pl;
     const char *why = "";
-    rc = make_plan(p, chip, 0, opts, device_occ, dev, false, &pl, &why);
-    if (rc != TG_OK)
-        return fail(rc, "%s", why);
+    // no options: a benchmark-mode winner for this problem, if one was recorded
+    tg_options tuned;
+    bool from_cache = false;
+    if (!opts && tune_lookup(dev, p, &tuned)) {
+        if (make_plan(p, chip, 0, &tuned, device_occ, dev, false, &pl, &why) == TG_OK) {
+            opts = &tuned;
+            from_cache = true;
+        }
+    }
+    if (!from_cache) {
+        rc = make_plan(p, chip, 0, opts, device_occ, dev, false, &pl, &why);
+        if (rc != TG_OK)
+            return fail(rc, "%s", why);
+    }
 
     void *ws = nullptr;
     bool own_ws = false;
@@ -510,7 +557,7 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
             ws = nullptr;
         }
         if (!ws) {
-            if (opts && opts->split_k > 1)
+            if (opts && opts->split_k > 1 && !from_cache)
                 return fail(TG_ERR_ARG, "forced split_k=%d needs %llu bytes of workspace",
                             opts->split_k, (unsigned long long)pl.workspace_bytes);
             // without the room: no K split, then no aligned copies either
@@ -605,6 +652,10 @@ int tg_gemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int trans, const tg
     Problem p = make_problem(M, N, K, dtype, trans, std::max<int64_t>(1, ta ? M : K),
                              std::max<int64_t>(1, tb ? K : N), std::max<int64_t>(1, N), true);
     const char *why = "";
+    tg_options tuned;
+    if (!opts && tune_lookup(dev, p, &tuned) &&
+        make_plan(p, device_chip(*dev), 0, &tuned, device_occ, dev, false, out, &why) == TG_OK)
+        return ok();
     rc = make_plan(p, device_chip(*dev), 0, opts, device_occ, dev, false, out, &why);
     if (rc != TG_OK)
         return fail(rc, "%s", why);
@@ -726,7 +777,32 @@ int tg_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
         return fail(TG_ERR_UNSUPPORTED, "no candidate plan ran");
     if (best_us)
         *best_us = best_t;
+    {
+        std::lock_guard<std::mutex> lk(g_tune_mu);
+        dev->tuned[tune_key(p)] = *best;
+    }
     return ok();
+}
+
+int tg_tune_cache_clear(void)
+{
+    DeviceInfo *dev = nullptr;
+    int rc = current_device(&dev);
+    if (rc != TG_OK)
+        return rc;
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    dev->tuned.clear();
+    return ok();
+}
+
+int64_t tg_tune_cache_size(void)
+{
+    DeviceInfo *dev = nullptr;
+    int rc = current_device(&dev);
+    if (rc != TG_OK)
+        return rc;
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    return (int64_t)dev->tuned.size();
 }
 
 int tg_device_cus(void)
