@@ -501,6 +501,63 @@ def align_sweep(out_path: str, reps: int = 5):
     print("\n".join(lines))
 
 
+def stream_k_compare(out_path: str, reps: int = 20):
+    """Stream-K against whole-tile plans: the planner's choice, forced stream-K
+    (split_k = TG_SPLIT_STREAM_K) and forced 256 x 256 tiles without a split, on
+    the M = 2304, K = 4096 quantization shapes that leave CUs idle, the bf16
+    6912 x 2048 x 4096 shape, and small-M/N, large-K products.  Each point is the
+    median of `reps` event-timed calls after 3 warm-ups, with a 256 MiB caller
+    workspace; inputs N(0, 1)/64 from a seeded device generator."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    device = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(device)
+    g = torch.Generator(device=device).manual_seed(1)
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=device)
+    tg.tune_cache_clear()
+
+    def timed(A, B, C, opts):
+        for _ in range(3):
+            tg.gemm(A, B, out=C, options=opts, workspace=ws, stream=stream.cuda_stream)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            tg.gemm(A, B, out=C, options=opts, workspace=ws, stream=stream.cuda_stream)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    lines = ["# Stream-K against whole-tile plans (one MI355X)", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"python3 bench.py --stream-k-compare {out_path}", "```", "",
+             "Each point: median of event-timed calls after warm-up, 256 MiB caller workspace;",
+             "TFLOP/s = 2MNK / time.", "",
+             "| Shape | dtype | Planner's plan | Planner TFLOP/s | Stream-K TFLOP/s (us) | 256x256, no split |",
+             "|---|---|---|---|---|---|"]
+    shapes = [(2304, n, 4096, torch.float16) for n in (2048, 3072, 3592, 4096, 4608, 5120, 5632)] + \
+             [(6912, 2048, 4096, torch.bfloat16), (1024, 1024, 4096, torch.float16),
+              (512, 512, 16384, torch.float16), (256, 256, 65536, torch.float16)]
+    for M, N, K, dt in shapes:
+        A = (torch.randn((M, K), generator=g, device=device) / 64).to(dt)
+        B = (torch.randn((K, N), generator=g, device=device) / 64).to(dt)
+        C = torch.empty((M, N), dtype=dt, device=device)
+        fl = 2.0 * M * N * K
+        pl = tg.plan_for(A, B)
+        t_p = timed(A, B, C, None)
+        t_sk = timed(A, B, C, dict(split_k=tg.TG_SPLIT_STREAM_K))
+        t_dp = timed(A, B, C, dict(tile_m=256, tile_n=256, split_k=1))
+        name = "bf16" if dt == torch.bfloat16 else "fp16"
+        lines.append(f"| {M}x{N}x{K} | {name} | {pl['tile_m']}x{pl['tile_n']} split {pl['split_k']} | "
+                     f"{fl / t_p / 1e9:.0f} | {fl / t_sk / 1e9:.0f} ({t_sk * 1e3:.1f}) | {fl / t_dp / 1e9:.0f} |")
+        log(lines[-1])
+        del A, B, C
+    lines.append("")
+    open(out_path, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def softmax_sweep(out_path: str, reps: int = 20):
     """Row softmax at M = 4096 over row lengths N = 256 .. 32768 and beyond (the
     shape of the Triton page's A100 figure, "OpenAI open-sources Triton",
@@ -578,6 +635,8 @@ def main():
                     help="with --sweep: also time tg_autotune's best plan at every point")
     ap.add_argument("--align-sweep", default=None,
                     help="run the K-alignment sweep, write its summary to this file, then exit")
+    ap.add_argument("--stream-k-compare", default=None,
+                    help="time stream-K against whole-tile plans, write the table to this file, then exit")
     ap.add_argument("--softmax-sweep", default=None,
                     help="run the M=4096 row-softmax sweep over N, write its summary to this file, then exit")
     ap.add_argument("--traffic-kernel", default=None,
@@ -614,6 +673,9 @@ def main():
         return
     if args.softmax_sweep:
         softmax_sweep(args.softmax_sweep)
+        return
+    if args.stream_k_compare:
+        stream_k_compare(args.stream_k_compare)
         return
     log("device", torch.cuda.get_device_name(0), "cus", tg.tg_device_cus())
 

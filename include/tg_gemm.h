@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 103
+#define TG_VERSION 104
 
 /* storage type of A, B and C */
 enum tg_dtype { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 };
@@ -102,6 +102,16 @@ typedef struct tg_epilogue {
     float beta;     /* scale of the old C, with TG_EPI_SCALE; 0 = C is not read */
 } tg_epilogue;
 
+/* tg_options.split_k / tg_plan.split_k value for stream-K: instead of whole
+ * tiles (or whole K splits) per workgroup, one workgroup per compute unit
+ * takes an equal run of all the tiles' K stages (32-deep), so a product with
+ * fewer tiles than compute units keeps every unit busy; tiles split between
+ * workgroups are summed, in K order, by a fix-up kernel into C.  256 x 256
+ * tiles, 16-bit 16-byte-aligned operands, fewer tiles than compute units
+ * ("Matrix Multiplication Background User's Guide", section 3.2: the tail
+ * wave; section 2.3: splitting K is the remedy libraries use). */
+#define TG_SPLIT_STREAM_K (-1)
+
 /* Optional planner overrides (NULL = all automatic).  A forced tile reproduces
  * the forced-tile measurements of "Matrix Multiplication Background User's
  * Guide", sections 3.1-3.2. */
@@ -109,28 +119,30 @@ typedef struct tg_options {
     int32_t path;    /* TG_PATH_AUTO, or a forced path */
     int32_t tile_m;  /* 0 = planner's choice, else a macro-tile height the path offers */
     int32_t tile_n;  /* 0 = planner's choice, else a macro-tile width */
-    int32_t split_k; /* 0 = planner's choice, 1 = no split, s > 1 = split K s ways */
+    int32_t split_k; /* 0 = planner's choice, 1 = no split, s > 1 = split K s ways,
+                        TG_SPLIT_STREAM_K = stream-K */
 } tg_options;
 
 /* What the planner decided, and the quantization figures behind it. */
 typedef struct tg_plan {
     int32_t path;        /* tg_path */
     int32_t tile_m, tile_n, tile_k;
-    int32_t split_k;     /* K-splits (1 = none) */
+    int32_t split_k;     /* K-splits (1 = none), or TG_SPLIT_STREAM_K */
     int32_t occupancy;   /* workgroups resident per compute unit */
     int32_t num_cus;     /* compute units the wave model used */
     int32_t vector_io;   /* 1 = 128-bit operand loads, 0 = element-wise, 2 = A and B first
                             copied into zero-padded 16-byte-aligned buffers at the start of
                             the workspace (K rounded up to 16 bytes), then 128-bit loads */
     int64_t tiles;       /* ceil(M/tile_m) * ceil(N/tile_n) */
-    int64_t workgroups;  /* tiles * split_k (MFMA/skinny), or the GEMV grid */
+    int64_t workgroups;  /* tiles * split_k (MFMA/skinny), the stream-K workgroups, or the GEMV grid */
     int64_t waves;       /* ceil(workgroups / (num_cus * occupancy)) */
     double tile_eff;     /* M*N / (tiles * tile_m * tile_n) */
     double wave_eff;     /* workgroups / (waves * num_cus * occupancy) */
     double pred_eff;     /* product of the two with the per-tile efficiency */
     double pred_us;      /* modelled run time, microseconds */
     double arith_intensity; /* 2MNK / (bytes of A, B and C), FLOP per byte */
-    uint64_t workspace_bytes; /* float32 split-K partials the plan needs */
+    uint64_t workspace_bytes; /* float32 split-K partials or stream-K pieces, and aligned
+                                 copies, the plan needs */
 } tg_plan;
 
 /* C = epi(alpha A . B + beta C) on the current HIP device.  epilogue may be

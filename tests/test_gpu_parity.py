@@ -449,6 +449,49 @@ def test_autotune_winner_is_cached_and_used():
         assert again[k] == heuristic[k]
 
 
+# ---------------------------------------------------------------- stream-K
+#
+# One workgroup per CU takes an equal run of all tiles' 32-deep K stages; tiles
+# split between workgroups are summed in K order by the fix-up kernel.  Cases:
+# 16 pieces per tile, a K tail stage with one stage per workgroup, ragged
+# tiles, every layout, two stages in all, and a K tail with 64 tiles.
+
+SK_CASES = [
+    # M, N, K, dtype, trans
+    (1024, 1024, 4096, F16, NN),
+    (512, 768, 1000, BF16, TN),
+    (296, 520, 2048, F16, NT),
+    (256, 512, 4096, BF16, TT),
+    (256, 256, 64, F16, NN),
+    (2048, 2048, 2080, F16, NN),
+]
+
+
+@pytest.mark.parametrize("case", SK_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}")
+def test_stream_k(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, dtype, trans = case
+    _say("case stream-K", case)
+    p = make_problem(M, N, K, dtype, trans, "normal", seed=61)
+    opts = dict(split_k=tg.TG_SPLIT_STREAM_K)
+    pl = tg.tg_gemm_plan(M, N, K, dtype, trans, opts)
+    assert pl["split_k"] == tg.TG_SPLIT_STREAM_K
+    r, _, _ = check_full(p, options=opts, out_pad=4)
+    assert r["ok"], (case, r)
+    r, _, _ = check_scaled(p, 0.75, -0.5, epilogue="leaky_relu", options=opts, c_seed=9)
+    assert r["ok"], (case, r)
+
+
+def test_stream_k_full_size_sampled():
+    """2304 x 4096 x 4096 (144 tiles on 256 CUs), in the configuration the
+    quantization sweep runs, checked at sampled outputs."""
+    import tiled_gemm_02_amd as tg
+    _say("case stream-K 2304x4096x4096")
+    p = make_problem(2304, 4096, 4096, F16, NN, "normal", seed=62)
+    r = check_sampled(p, options=dict(split_k=tg.TG_SPLIT_STREAM_K))
+    assert r["ok"], r
+
+
 # ---------------------------------------------------------------- aligned copies
 #
 # Operands off the 16-byte grid (K odd, padded leading dimensions) in products

@@ -93,9 +93,14 @@ def test_mi355x_plans():
     # K == 0 and empty outputs are quick returns
     assert tg.tg_plan_model(64, 64, 0, F16)["path_name"] == "none"
     assert tg.tg_plan_model(0, 64, 64, F16)["path_name"] == "none"
-    # small M and N with large K split K
+    # small M and N with large K split K (whole splits, or stream-K's runs)
     p = tg.tg_plan_model(256, 256, 65536, F16)
-    assert p["split_k"] > 1 and p["workspace_bytes"] == p["split_k"] * 256 * 256 * 4
+    if p["split_k"] == tg.TG_SPLIT_STREAM_K:
+        assert p["workgroups"] == 256 and p["workspace_bytes"] == 2 * 256 * 256 * 256 * 4
+    else:
+        assert p["split_k"] > 1 and p["workspace_bytes"] == p["split_k"] * 256 * 256 * 4
+    p = tg.tg_plan_model(256, 256, 65536, F16, options=dict(split_k=16))
+    assert p["split_k"] == 16 and p["workspace_bytes"] == 16 * 256 * 256 * 4
     # on 256 CUs a forced 256x128 tile steps from one to two waves between N = 3584 and 3592
     f = dict(tile_m=256, tile_n=128, split_k=1)
     a = tg.tg_plan_model(2304, 3584, 4096, F16, occupancy=1, options=f)
@@ -147,3 +152,27 @@ def test_unaligned_operands_are_copied_when_it_pays():
     sk = tg.tg_plan_model(8192, 96, 8191, F, tg.TG_NN, options=dict(path="skinny"))
     assert sk["vector_io"] == 2 and sk["path_name"] == "skinny"
 
+
+
+def test_stream_k_plans():
+    """Stream-K (split_k = TG_SPLIT_STREAM_K): one workgroup per CU over all
+    tiles' 32-deep K stages, 256 x 256 tiles, two float32 tile pieces of
+    workspace per workgroup; only with fewer tiles than CUs."""
+    F = tg.TG_F16
+    SK = tg.TG_SPLIT_STREAM_K
+    p = tg.tg_plan_model(2304, 4096, 4096, F, tg.TG_NN, options=dict(split_k=SK))
+    assert p["split_k"] == SK and (p["tile_m"], p["tile_n"]) == (256, 256)
+    assert p["tiles"] == 9 * 16 and p["workgroups"] == 256
+    assert p["workspace_bytes"] == 2 * 256 * 256 * 256 * 4
+    # fewer K stages than CUs: one workgroup per stage
+    q = tg.tg_plan_model(256, 256, 64, F, tg.TG_NN, options=dict(split_k=SK))
+    assert q["workgroups"] == 2
+    # not offered: float32, unaligned sizes, as many tiles as CUs, other tiles
+    for args, opts in [((1024, 1024, 4096, tg.TG_F32), dict(split_k=SK)),
+                       ((256, 252, 1024, F), dict(split_k=SK)),
+                       ((8192, 8192, 8192, F), dict(split_k=SK)),
+                       ((1024, 1024, 4096, F), dict(split_k=SK, tile_m=128, tile_n=128))]:
+        with pytest.raises(tg.TgError):
+            tg.tg_plan_model(*args, tg.TG_NN, options=opts)
+    with pytest.raises(tg.TgError):
+        tg.tg_plan_model(1024, 1024, 4096, F, tg.TG_NN, options=dict(split_k=-2))

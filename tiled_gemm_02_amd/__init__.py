@@ -33,6 +33,7 @@ class TgError(RuntimeError):
 
 
 TG_EPI_SCALE = 1   # tg_epilogue.flags: use alpha and beta
+TG_SPLIT_STREAM_K = -1   # tg_options.split_k: stream-K
 
 
 class Epilogue(ctypes.Structure):

@@ -31,6 +31,15 @@ hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, const Mfm
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_mfma2_sk(int dtype, int trans, const MfmaArgs &a, hipStream_t s)
+{
+    switch (dtype) {
+    case TG_F16: return launch_mfma2_sk_f16(trans, a, s);
+    case TG_BF16: return launch_mfma2_sk_bf16(trans, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s)
 {
     switch (dtype) {
@@ -411,11 +420,6 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.M = (int)p.M;
         a.N = (int)p.N;
         a.K = (int)p.K;
-        const int BK = pl.tile_k;
-        int64_t kps = (p.K + pl.split_k - 1) / pl.split_k;
-        kps = (kps + BK - 1) / BK * BK;
-        a.kps = (int)kps;
-        a.splits = pl.split_k;
         a.tiles_m = (int)((p.M + pl.tile_m - 1) / pl.tile_m);
         a.tiles_n = (int)((p.N + pl.tile_n - 1) / pl.tile_n);
         a.oe = oe;
@@ -423,6 +427,27 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.c_vec = (p.ldc % 4 == 0) && (((uintptr_t)C) % (4 * cb) == 0);
         a.rows_a = (int)(rows_a ? rows_a : p.M);
         a.cols_b = (int)(cols_b ? cols_b : p.N);
+        if (pl.split_k == TG_SPLIT_STREAM_K) {
+            // one workgroup per CU over all tiles' 32-deep K stages, then the fix-up
+            a.sk_ipt = (int)((p.K + kStreamKStage - 1) / kStreamKStage);
+            a.sk_total = (int64_t)a.tiles_m * a.tiles_n * a.sk_ipt;
+            // fix-up bands: about 1024 workgroups over the tiles (1 to 16 rows each)
+            const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+            a.sk_rows = 16;
+            while (a.sk_rows > 1 && tiles * (256 / a.sk_rows) < 1024)
+                a.sk_rows /= 2;
+            a.splits = (int)pl.workgroups;
+            a.kps = (int)p.K;
+            e = launch_mfma2_sk(p.dtype, p.trans, a, s);
+            if (e != hipSuccess)
+                return fail(TG_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+            return TG_OK;
+        }
+        const int BK = pl.tile_k;
+        int64_t kps = (p.K + pl.split_k - 1) / pl.split_k;
+        kps = (kps + BK - 1) / BK * BK;
+        a.kps = (int)kps;
+        a.splits = pl.split_k;
         if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, p.M, p.N, p.K, p.lda, p.ldb))
             e = launch_mfma2(p.dtype, p.trans, pl.tile_m, pl.tile_n, a, s);
         else
@@ -557,7 +582,7 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
             ws = nullptr;
         }
         if (!ws) {
-            if (opts && opts->split_k > 1 && !from_cache)
+            if (opts && (opts->split_k > 1 || opts->split_k == TG_SPLIT_STREAM_K) && !from_cache)
                 return fail(TG_ERR_ARG, "forced split_k=%d needs %llu bytes of workspace",
                             opts->split_k, (unsigned long long)pl.workspace_bytes);
             // without the room: no K split, then no aligned copies either
@@ -725,6 +750,7 @@ int tg_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
         for (int sp : splits)
             cands.push_back(tg_options{TG_PATH_MFMA, menu[i].bm, menu[i].bn, sp});
     cands.push_back(tg_options{TG_PATH_MFMA, 64, 64, 1});   // the element-wise tile
+    cands.push_back(tg_options{TG_PATH_MFMA, 256, 256, TG_SPLIT_STREAM_K});
     for (int sp : {1, 2, 4})
         cands.push_back(tg_options{TG_PATH_SKINNY, 0, 0, sp});
 

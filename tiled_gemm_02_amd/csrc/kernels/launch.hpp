@@ -20,6 +20,9 @@ int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec);
 // The LDS-DMA kernel for 16-bit, 16-byte-aligned operands (same tiles).
 hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s);
 int mfma2_occupancy(int dtype, int trans, int bm, int bn);
+// Stream-K with 256 x 256 tiles on a.splits workgroups (16-bit, aligned), then
+// the fix-up of the split tiles; a.ws holds 2 * a.splits float32 tiles.
+hipError_t launch_mfma2_sk(int dtype, int trans, const MfmaArgs &a, hipStream_t s);
 // C (M x N) = out(sum of `splits` float32 planes of partials, rows wsld apart)
 hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int64_t wsld, int64_t plane,
                                 int M, int N, void *C, int64_t ldc, const OutEpi &oe, int c_vec,
@@ -56,6 +59,7 @@ hipError_t launch_softmax(int dtype, int q, int c, bool vec, const SoftmaxArgs &
     hipError_t launch_skinny_##NAME(bool trans_b, const SkinnyArgs &a, hipStream_t s);           \
     hipError_t launch_mfma2_##NAME(int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s); \
     int mfma2_occupancy_##NAME(int trans, int bm, int bn);                                       \
+    hipError_t launch_mfma2_sk_##NAME(int trans, const MfmaArgs &a, hipStream_t s);              \
     hipError_t launch_softmax_##NAME(int q, int c, bool vec, const SoftmaxArgs &a, hipStream_t s);
 
 TG_DECLARE_TYPE_LAUNCHERS(f16)

@@ -51,7 +51,28 @@ struct MfmaArgs {
     int c_vec;        // 1: C rows are 16-byte aligned and ldc % 4 == 0
     int rows_a;       // rows of A(i, k) the loads may touch, >= M (padded copies: M rounded up)
     int cols_b;       // columns of B(k, j) the loads may touch, >= N
+    // stream-K schedule (ping-pong kernel only): the tiles' K stages laid end
+    // to end, sk_total = tiles * sk_ipt, cut into gridDim.x equal runs
+    int sk_ipt;       // K stages per tile
+    int sk_rows;      // fix-up: tile rows per workgroup
+    int64_t sk_total;
 };
+
+// Stream-K bookkeeping shared by the kernel and its fix-up: workgroup g of G
+// owns stages [sk_start(g), sk_start(g + 1)) of the end-to-end sequence.
+__host__ __device__ inline int64_t sk_start(int64_t g, int64_t total, int64_t G)
+{
+    const int64_t base = total / G, rem = total % G;
+    return g * base + (g < rem ? g : rem);
+}
+
+// The workgroup that owns stage `it`.
+__host__ __device__ inline int64_t sk_owner(int64_t it, int64_t total, int64_t G)
+{
+    const int64_t base = total / G, rem = total % G;
+    const int64_t big = rem * (base + 1);
+    return it < big ? it / (base + 1) : rem + (it - big) / base;
+}
 
 // 16-byte-chunk XOR swizzle of an LDS row (8 chunks per row).
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }

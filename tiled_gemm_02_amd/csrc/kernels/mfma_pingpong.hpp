@@ -4,7 +4,7 @@
 // Tiling ("Matrix Multiplication Background User's Guide", section 2.1): one
 // 256 x 256 tile of C per workgroup, eight wave64s in a 2 x 4 grid, each wave
 // owning 128 x 64 of the tile (8 x 4 blocks of v_mfma_f32_16x16x32, fp32
-// accumulate, 128 accumulator registers).  K advances in 32-deep stages (one
+// accumulate, 128 accumulator registers per lane).  K advances in 32-deep stages (one
 // MFMA K block each, 32 KiB of LDS), S of them buffered, copied by the LDS-DMA
 // path of mfma_gemm3.hpp (K-contiguous rows of 64 bytes).
 //
@@ -80,7 +80,7 @@ __device__ __forceinline__ uint32_t mn32_base(uint32_t st, int ks, int h, int la
     return st + (uint32_t)((k * CH + c) * 16 + (n & 7) * 2);
 }
 
-template <typename Tr, int S, int MI, bool TA, bool TB>
+template <typename Tr, int S, int MI, bool TA, bool TB, bool SK = false>
 __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -108,12 +108,14 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
     const int grp = wm;            // group = row half of the tile
     const int gwave = wave & 3;    // wave index within its group
 
-    int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const int z = blockIdx.y;
-    const int kbeg = z * p.kps;
-    const int klen = max(0, min(p.K, kbeg + p.kps) - kbeg);
+    // One work item: the K range [kbeg, kbeg + klen) of the tile at (m0, n0),
+    // stored to C (through the output transform), to split z's float32 plane
+    // of the workspace (K split), or as a tile-local float32 partial at Wt
+    // (stream-K).  Every wave executes the same barriers, so items can follow
+    // one another in a workgroup: all LDS reads of an item are consumed before
+    // its last barrier.
+    auto item = [&](const int m0, const int n0, const int z, const int kbeg, const int klen,
+                    float *const Wt) {
     const int nfull = klen / BKS;
     const int has_tail = (klen % BKS) != 0;
     const int nst = nfull + has_tail;
@@ -255,8 +257,12 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
                     for (int j = 0; j < FN; ++j) {
+                        // 16 x 16 blocks: the compiler's own MFMA, accumulators in
+                        // VGPRs (measured as fast as tied AGPR accumulators, with
+                        // no spills, and the compiler sees and covers every
+                        // hazard of a register it moves)
                         if constexpr (MI == 16)
-                            mfma_tied<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
+                            mfma_chunk<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
                         else
                             mfma32_tied<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
                     }
@@ -289,16 +295,23 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
                 lds_barrier();
             }
         }
-        mfma_drain();
+        if constexpr (MI != 16)
+            mfma_drain();   // tied asm accumulators: the hazard the compiler cannot see
     }
 
     // ---- epilogue: each lane holds runs of 4 consecutive columns of C
     T *C = (T *)p.C;
     float *W = p.ws + (int64_t)z * p.M * p.N;
     auto store4 = [&](int m, int n, const f32x4 &v) {
+        if constexpr (SK) {
+            if (Wt) {   // the whole tile, rows and columns past M and N included
+                *(f32x4 *)(Wt + (m - m0) * BN + (n - n0)) = v;
+                return;
+            }
+        }
         if (m >= p.M || n >= p.N)
             return;
-        if (p.splits > 1) {
+        if (!SK && p.splits > 1) {
             float *dst = W + (int64_t)m * p.N + n;
             if (n + 3 < p.N && (p.N & 3) == 0) {
                 *(f32x4 *)dst = v;
@@ -327,9 +340,90 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
                 }
             }
         }
+    };
+
+    if constexpr (!SK) {
+        int tm, tn;
+        tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+        const int z = blockIdx.y;
+        const int kbeg = z * p.kps;
+        item(tm * BM, tn * BN, z, kbeg, max(0, min(p.K, kbeg + p.kps) - kbeg), nullptr);
+    } else {
+        // stream-K: this workgroup's run of the tiles' stages, one item per
+        // tile it touches (at most two: runs are shorter than a tile); a
+        // whole tile goes straight to C, a piece to slot 2 g + j (g: the run)
+        // run g of the sequence goes to workgroup ids that share an XCD (ids
+        // go round-robin over the 8 XCDs): each XCD takes a contiguous
+        // stretch of runs, i.e. of neighbouring tiles
+        const int G = gridDim.x;
+        const int q = G >> 3, rr = G & 7, x = blockIdx.x & 7;
+        const int64_t g = x * q + min(x, rr) + (blockIdx.x >> 3);
+        const int64_t beg = sk_start(g, p.sk_total, G), end = sk_start(g + 1, p.sk_total, G);
+        int j = 0;
+        for (int64_t it = beg; it < end; ++j) {
+            const int t = (int)(it / p.sk_ipt);
+            const int s0 = (int)(it - (int64_t)t * p.sk_ipt);
+            const int s1 = (int)min<int64_t>(p.sk_ipt, s0 + (end - it));
+            int tm, tn;
+            tile_coords(t, p.tiles_m, p.tiles_n, tm, tn);
+            const bool whole = s0 == 0 && s1 == p.sk_ipt;
+            float *Wt = whole ? nullptr : p.ws + (2 * g + j) * (int64_t)(BM * BN);
+            const int kbeg = s0 * BKS;
+            item(tm * BM, tn * BN, 0, kbeg, min(p.K, s1 * BKS) - kbeg, Wt);
+            it += s1 - s0;
+        }
+    }
 #else
     (void)p;
 #endif
+}
+
+// Stream-K fix-up.  Tile t whose stages were split between workgroups
+// g0 .. g1 gets the sum of their float32 pieces, in stage order (g0 first),
+// through the output transform; a tile one workgroup finished is already in
+// C.  Run g's piece of its j-th tile is slot 2 g + j.  Grid: x = tiles,
+// y = bands of p.sk_rows rows of a tile; the pieces of an element are loaded
+// eight at a time and added in order.
+template <typename Tr, int BM, int BN>
+__global__ __launch_bounds__(256) void sk_fixup_kernel(MfmaArgs p)
+{
+    using T = typename Tr::T;
+    constexpr int U = 8;
+    const int t = blockIdx.x;
+    const int64_t G = p.splits;   // workgroups of the stream-K launch
+    const int64_t g0 = sk_owner((int64_t)t * p.sk_ipt, p.sk_total, G);
+    const int64_t g1 = sk_owner((int64_t)(t + 1) * p.sk_ipt - 1, p.sk_total, G);
+    if (g0 == g1)
+        return;
+    int tm, tn;
+    tile_coords(t, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    T *C = (T *)p.C;
+    constexpr int NQ = BN / 4;
+    for (int idx = threadIdx.x; idx < p.sk_rows * NQ; idx += 256) {
+        const int r = blockIdx.y * p.sk_rows + idx / NQ, c = (idx % NQ) * 4;
+        const int m = m0 + r, n = n0 + c;
+        if (m >= p.M || n >= p.N)
+            continue;
+        const float *base = p.ws + r * BN + c;
+        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int64_t g = g0; g <= g1; g += U) {
+            f32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t gg = g + u;
+                if (gg <= g1) {
+                    const int64_t j = t - sk_start(gg, p.sk_total, G) / p.sk_ipt;
+                    v[u] = *(const f32x4 *)(base + (2 * gg + j) * (int64_t)(BM * BN));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (g + u <= g1)
+                    s += v[u];
+        }
+        store_out4<Tr>(C + (int64_t)m * p.ldc + n, s, p.N - n, p.c_vec && n + 3 < p.N, p.oe);
+    }
 }
 
 }  // namespace tg

@@ -247,6 +247,55 @@ static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int
     return c;
 }
 
+// Stream-K on 256 x 256 tiles (the ping-pong kernel: 16-bit, 16-byte-aligned
+// operands, 32-deep K stages): G = one workgroup per CU shares the tiles' K
+// stages evenly.  Only for fewer tiles than CUs, where a tile wave leaves CUs
+// idle; each run is then shorter than a tile and touches at most two tiles.
+static bool sk_ok(const Problem &p, const Chip &chip)
+{
+    const int64_t tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    return vec_ok(p) && p.dtype != TG_F32 && p.lda <= (1 << 22) && p.ldb <= (1 << 22) &&
+           find_tile(p.dtype, 256, 256) != nullptr && tiles < chip.num_cus;
+}
+
+// Measured on MI355X (fp16, 2304 x N x 4096, 72-216 tiles): a stream-K stage
+// takes about 1.9x a whole-tile stage.  The runs of one XCD sit at unrelated
+// K offsets of their tiles, so the panel reuse in L2 that a wave of whole
+// tiles gets (neighbouring tiles at the same K) is lost; the fix-up then reads
+// every piece once at about 70 % of the HBM rate.
+constexpr double kStreamKStageCost = 1.9;
+constexpr double kStreamKFixupHbm = 0.7;
+
+static Cand price_sk(const Problem &p, const Chip &chip, double eff)
+{
+    Cand c{};
+    c.bm = c.bn = 256;
+    c.occ = 1;
+    c.eff = eff;
+    c.s = -1;
+    c.tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    const int64_t ipt = (p.K + kStreamKStage - 1) / kStreamKStage;
+    const int64_t total = c.tiles * ipt;
+    const int64_t G = std::min<int64_t>(chip.num_cus, total);
+    c.units = G;
+    c.waves = 1;
+    c.kps = kStreamKStage;
+    const double t_stage =
+        kStreamKStageCost * (2.0 * 256 * 256 * kStreamKStage) / (flop_rate_cu(chip, p.dtype) * eff);
+    const double tile_f32 = 256.0 * 256.0 * 4.0;
+    // longest run, then the last pieces written by every workgroup at once,
+    // then the fix-up: every piece read once, the split tiles' C written
+    const double pieces = (double)std::min<int64_t>(2 * G, G + c.tiles);
+    double t = (double)((total + G - 1) / G) * t_stage;
+    t = std::max(t, alg_bytes(p) / (chip.hbm_gbs * 1e9));
+    t += (double)G * tile_f32 / (chip.hbm_gbs * 1e9);
+    t += (pieces * tile_f32 + (double)p.M * p.N * elem_bytes(p.dtype)) /
+             (kStreamKFixupHbm * chip.hbm_gbs * 1e9) +
+         chip.launch_us * 1e-6;
+    c.t = t;
+    return c;
+}
+
 static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg_options *opts,
                      OccFn occ_fn, void *occ_ctx, bool model, tg_plan *out, const char **why)
 {
@@ -284,9 +333,23 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
         menu = f;
         nmenu = 1;
     }
+    const bool force_sk = opts && opts->split_k == TG_SPLIT_STREAM_K;
+    if (opts && opts->split_k < 0 && !force_sk) {
+        *why = "split_k must be 0, positive, or TG_SPLIT_STREAM_K";
+        return TG_ERR_ARG;
+    }
+    const bool tile_256 = !(opts && (opts->tile_m > 0 || opts->tile_n > 0)) ||
+                          (opts->tile_m == 256 && opts->tile_n == 256);
+    if (force_sk && !(tile_256 && sk_ok(p, chip))) {
+        *why = "stream-K needs 16-bit, 16-byte-aligned operands with 256 x 256 tiles, "
+               "and fewer tiles than compute units";
+        return TG_ERR_UNSUPPORTED;
+    }
     int splits[16];
     int nsplit = 0;
-    if (opts && opts->split_k > 0) {
+    if (force_sk) {
+        // priced below
+    } else if (opts && opts->split_k > 0) {
         splits[nsplit++] = opts->split_k;
     } else {
         const int cand[] = {1, 2, 3, 4, 6, 8, 12, 16};
@@ -296,7 +359,15 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
     }
     bool have = false;
     Cand best{};
-    for (int i = 0; i < nmenu; ++i) {
+    // offered (not forced) only where each tile is shared by at most eight
+    // workgroups: more pieces per tile cost more in the fix-up than they save
+    const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    if (tile_256 && !(opts && opts->split_k > 0) && sk_ok(p, chip) &&
+        (force_sk || tiles256 * 8 >= chip.num_cus)) {
+        best = price_sk(p, chip, find_tile(p.dtype, 256, 256)->eff);
+        have = true;
+    }
+    for (int i = 0; i < nmenu && !force_sk; ++i) {
         const TileSpec &ts = menu[i];
         int occ = occupancy > 0 ? occupancy
                                 : (occ_fn ? occ_fn(p.dtype, p.trans, ts.bm, ts.bn, vec, occ_ctx)
@@ -336,6 +407,11 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
     out->pred_us = best.t * 1e6;
     out->pred_eff = (2.0 * p.M * p.N * p.K / best.t) / chip_peak(chip, p.dtype);
     out->workspace_bytes = best.s > 1 ? (uint64_t)best.s * p.M * p.N * 4u : 0;
+    if (best.s == TG_SPLIT_STREAM_K) {
+        out->tile_k = kStreamKStage;
+        out->wave_eff = (double)best.units / chip.num_cus;
+        out->workspace_bytes = (uint64_t)2 * best.units * 256 * 256 * 4;
+    }
     return TG_OK;
 }
 

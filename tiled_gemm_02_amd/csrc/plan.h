@@ -94,6 +94,10 @@ inline int elem_bytes(int dtype) { return dtype == TG_F32 ? 4 : 2; }
 // q * 64 * c * chunk_elems) that holds the row, or q = c = 0 for the two-pass
 // long-row kernel (N above kSoftmaxMaxResident).
 constexpr int64_t kSoftmaxMaxResident = 32768;
+
+// K depth of one stage of the 256 x 256 ping-pong kernel: the unit in which
+// stream-K shares the tiles' K loops between workgroups.
+constexpr int kStreamKStage = 32;
 void softmax_shape(int dtype, int64_t N, int *q, int *c);
 
 }  // namespace tg
