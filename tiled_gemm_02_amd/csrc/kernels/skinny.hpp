@@ -270,7 +270,9 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
                     for (int i = 0; i < MB; ++i)
 #pragma unroll
                         for (int j = 0; j < NBK; ++j)
-                            mfma_tied<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
+                            // the compiler's MFMA (accumulators in VGPRs): 6 % faster
+                            // here than tied AGPR accumulators
+                            mfma_chunk<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
             }
         }
     };
@@ -279,7 +281,6 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
         return;
     }
     b_loop(std::true_type{});
-    mfma_drain();
 
     // ---- epilogue: lane holds C[m][n .. n + 3] of each of its blocks
 #pragma unroll
