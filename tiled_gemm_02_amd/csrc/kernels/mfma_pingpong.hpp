@@ -116,230 +116,233 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
     // its last barrier.
     auto item = [&](const int m0, const int n0, const int z, const int kbeg, const int klen,
                     float *const Wt) {
-    const int nfull = klen / BKS;
-    const int has_tail = (klen % BKS) != 0;
-    const int nst = nfull + has_tail;
+        const int nfull = klen / BKS;
+        const int has_tail = (klen % BKS) != 0;
+        const int nst = nfull + has_tail;
 
-    OpA oa;
-    OpB ob;
-    if (grp == 0)
-        oa.init((const uint16_t *)p.A, p.lda, p.rows_a, m0, kbeg, gwave, lane);
-    else
-        ob.init((const uint16_t *)p.B, p.ldb, p.cols_b, n0, kbeg, gwave, lane);
-    const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
-    // this group's operand of processing stage t into its buffer: the K tail
-    // (stage 0 when there is one) through registers, the rest by DMA
-    auto issue = [&](int t) {
-        const int slot = t % S;
-        if (has_tail && t == 0) {
-            char *st = lds + slot * STAGE;
-            const int krel = klen - nfull * BKS;
-            if (grp == 0)
-                oa.tail(nfull, krel, st, gwave, lane);
-            else
-                ob.tail(nfull, krel, st + A_BYTES, gwave, lane);
-        } else if (grp == 0) {
-            oa.dma(t - has_tail, lds_base + slot * STAGE, gwave);
-        } else {
-            ob.dma(t - has_tail, lds_base + slot * STAGE + A_BYTES, gwave);
-        }
-    };
-    // Wait until this wave's copies of stage t have landed, stages up to
-    // `last` having been issued: the younger stages (all DMA) may stay in
-    // flight.  `lds` also waits for this wave's LDS traffic (the prologue's
-    // register-path writes).
-    auto wait_stage = [&](int t, int last, bool lds_too) {
-        const int younger = max(0, min(last - t, S - 2));
-        if (lds_too) {
-            if (S >= 5 && younger >= 3)
-                wait_vm_lgkm<(S >= 5 ? 3 : 0) * NDMA>();
-            else if (S >= 4 && younger == 2)
-                wait_vm_lgkm<(S >= 4 ? 2 : 0) * NDMA>();
-            else if (younger == 1)
-                wait_vm_lgkm<NDMA>();
-            else
-                wait_vm_lgkm<0>();
-        } else {
-            if (S >= 5 && younger >= 3)
-                wait_vm<(S >= 5 ? 3 : 0) * NDMA>();
-            else if (S >= 4 && younger == 2)
-                wait_vm<(S >= 4 ? 2 : 0) * NDMA>();
-            else if (younger == 1)
-                wait_vm<NDMA>();
-            else
-                wait_vm<0>();
-        }
-    };
-
-    // fragment reads of one stage: (K step, row block) for A, (K step,
-    // column block) for B
-    uint32_t mnA[KS][2], mnB[KS][2];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if constexpr (MI == 16) {
-                mnA[ks][h] = mn3_base<BM / 8>(lds_base, 0, h, lane);
-                mnB[ks][h] = mn3_base<BN / 8>(lds_base + A_BYTES, 0, h, lane);
+        OpA oa;
+        OpB ob;
+        if (grp == 0)
+            oa.init((const uint16_t *)p.A, p.lda, p.rows_a, m0, kbeg, gwave, lane);
+        else
+            ob.init((const uint16_t *)p.B, p.ldb, p.cols_b, n0, kbeg, gwave, lane);
+        const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+        // this group's operand of processing stage t into its buffer: the K tail
+        // (stage 0 when there is one) through registers, the rest by DMA
+        auto issue = [&](int t) {
+            const int slot = t % S;
+            if (has_tail && t == 0) {
+                char *st = lds + slot * STAGE;
+                const int krel = klen - nfull * BKS;
+                if (grp == 0)
+                    oa.tail(nfull, krel, st, gwave, lane);
+                else
+                    ob.tail(nfull, krel, st + A_BYTES, gwave, lane);
+            } else if (grp == 0) {
+                oa.dma(t - has_tail, lds_base + slot * STAGE, gwave);
             } else {
-                mnA[ks][h] = mn32_base<BM / 8>(lds_base, ks, h, lane);
-                mnB[ks][h] = mn32_base<BN / 8>(lds_base + A_BYTES, ks, h, lane);
-            }
-        }
-    auto read_a = [&](const char *st, int ks, int i) -> u32x4 {
-        const int r0 = wm * WM + MI * i;
-        if constexpr (!TA) {
-            if constexpr (MI == 16)
-                return frag3_kc<BKS / 8>(st, r0, 0, lane);
-            else
-                return frag32_kc(st, r0, ks, lane);
-        } else {
-            const uint32_t so = (uint32_t)(st - lds);
-            return frag3_mn<BM / 8>(mnA[ks][0] + so, mnA[ks][1] + so, r0);
-        }
-    };
-    auto read_b = [&](const char *st, int ks, int j) -> u32x4 {
-        const int c0 = wn * WN + MI * j;
-        if constexpr (TB) {
-            if constexpr (MI == 16)
-                return frag3_kc<BKS / 8>(st + A_BYTES, c0, 0, lane);
-            else
-                return frag32_kc(st + A_BYTES, c0, ks, lane);
-        } else {
-            const uint32_t so = (uint32_t)(st - lds);
-            return frag3_mn<BN / 8>(mnB[ks][0] + so, mnB[ks][1] + so, c0);
-        }
-    };
-
-    using AccT = typename std::conditional<MI == 16, f32x4, f32x16>::type;
-    AccT acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            acc[i][j] = AccT{};
-
-    if (nst > 0) {
-        u32x4 fa[KS][FM], fb[KS][FN];   // one stage of fragments
-
-        // stages 0 .. S - 2 come first; stage b + S - 2 follows with stage b
-        const int pro = min(nst, S - 1);
-#pragma unroll
-        for (int t = 0; t < S - 1; ++t)
-            if (t < pro)
-                issue(t);
-        wait_stage(0, pro - 1, true);
-        lds_barrier();
-
-        // load stage b into (fa, fb), after refilling the buffer of stage
-        // b - 2 with stage b + S - 2; the reads are left in flight
-        auto load = [&](int b) {
-            if (b >= 1 && b + S - 2 < nst)
-                issue(b + S - 2);
-            const char *st = lds + (b % S) * STAGE;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    fb[ks][j] = read_b(st, ks, j);
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    fa[ks][i] = read_a(st, ks, i);
+                ob.dma(t - has_tail, lds_base + slot * STAGE + A_BYTES, gwave);
             }
         };
-        // multiply the stage in (fa, fb): 32 (16 x 16) or 16 (32 x 32) MFMAs
-        // with nothing to wait for
-        auto multiply = [&]() {
-            __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        // 16 x 16 blocks: the compiler's own MFMA, accumulators in
-                        // VGPRs (measured as fast as tied AGPR accumulators, with
-                        // no spills, and the compiler sees and covers every
-                        // hazard of a register it moves)
-                        if constexpr (MI == 16)
-                            mfma_chunk<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
-                        else
-                            mfma32_tied<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
-                    }
-            __builtin_amdgcn_s_setprio(0);
-        };
-        // before the barrier that opens phase 2b + 2 (stage b + 1 first read)
-        auto sync_next = [&](int b) {
-            if (b + 1 < nst)
-                wait_stage(b + 1, min(nst - 1, b + S - 2), false);
-        };
-        // Each group runs its own straight-line loop (no role branches, so
-        // the accumulators stay in their AGPRs); both execute 2 nst + 1
-        // barriers, group 1 one phase behind group 0.
-        if (grp == 0) {
-            for (int b = 0; b < nst; ++b) {
-                load(b);
-                lds_barrier();
-                multiply();
-                sync_next(b);
-                lds_barrier();
+        // Wait until this wave's copies of stage t have landed, stages up to
+        // `last` having been issued: the younger stages (all DMA) may stay in
+        // flight.  `lds` also waits for this wave's LDS traffic (the prologue's
+        // register-path writes).
+        auto wait_stage = [&](int t, int last, bool lds_too) {
+            const int younger = max(0, min(last - t, S - 2));
+            if (lds_too) {
+                if (S >= 5 && younger >= 3)
+                    wait_vm_lgkm<(S >= 5 ? 3 : 0) * NDMA>();
+                else if (S >= 4 && younger == 2)
+                    wait_vm_lgkm<(S >= 4 ? 2 : 0) * NDMA>();
+                else if (younger == 1)
+                    wait_vm_lgkm<NDMA>();
+                else
+                    wait_vm_lgkm<0>();
+            } else {
+                if (S >= 5 && younger >= 3)
+                    wait_vm<(S >= 5 ? 3 : 0) * NDMA>();
+                else if (S >= 4 && younger == 2)
+                    wait_vm<(S >= 4 ? 2 : 0) * NDMA>();
+                else if (younger == 1)
+                    wait_vm<NDMA>();
+                else
+                    wait_vm<0>();
             }
-            lds_barrier();
-        } else {
-            lds_barrier();
-            for (int b = 0; b < nst; ++b) {
-                load(b);
-                sync_next(b);
-                lds_barrier();
-                multiply();
-                lds_barrier();
-            }
-        }
-        if constexpr (MI != 16)
-            mfma_drain();   // tied asm accumulators: the hazard the compiler cannot see
-    }
+        };
 
-    // ---- epilogue: each lane holds runs of 4 consecutive columns of C
-    T *C = (T *)p.C;
-    float *W = p.ws + (int64_t)z * p.M * p.N;
-    auto store4 = [&](int m, int n, const f32x4 &v) {
-        if constexpr (SK) {
-            if (Wt) {   // the whole tile, rows and columns past M and N included
-                *(f32x4 *)(Wt + (m - m0) * BN + (n - n0)) = v;
-                return;
-            }
-        }
-        if (m >= p.M || n >= p.N)
-            return;
-        if (!SK && p.splits > 1) {
-            float *dst = W + (int64_t)m * p.N + n;
-            if (n + 3 < p.N && (p.N & 3) == 0) {
-                *(f32x4 *)dst = v;
-            } else {
+        // fragment reads of one stage: (K step, row block) for A, (K step,
+        // column block) for B
+        uint32_t mnA[KS][2], mnB[KS][2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (n + e < p.N)
-                        dst[e] = v[e];
-            }
-            return;
-        }
-        store_out4<Tr>(C + (int64_t)m * p.ldc + n, v, p.N - n, p.c_vec && n + 3 < p.N, p.oe);
-    };
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            if constexpr (MI == 16) {
-                // C[m0 + .. + (lane & 15)][n0 + .. + 4 (lane >> 4) .. + 3]
-                store4(m0 + wm * WM + 16 * i + (lane & 15), n0 + wn * WN + 16 * j + 4 * (lane >> 4), acc[i][j]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    store4(m0 + wm * WM + 32 * i + (lane & 31), n0 + wn * WN + 32 * j + 8 * q + 4 * (lane >> 5), v);
+            for (int h = 0; h < 2; ++h) {
+                if constexpr (MI == 16) {
+                    mnA[ks][h] = mn3_base<BM / 8>(lds_base, 0, h, lane);
+                    mnB[ks][h] = mn3_base<BN / 8>(lds_base + A_BYTES, 0, h, lane);
+                } else {
+                    mnA[ks][h] = mn32_base<BM / 8>(lds_base, ks, h, lane);
+                    mnB[ks][h] = mn32_base<BN / 8>(lds_base + A_BYTES, ks, h, lane);
                 }
             }
+        auto read_a = [&](const char *st, int ks, int i) -> u32x4 {
+            const int r0 = wm * WM + MI * i;
+            if constexpr (!TA) {
+                if constexpr (MI == 16)
+                    return frag3_kc<BKS / 8>(st, r0, 0, lane);
+                else
+                    return frag32_kc(st, r0, ks, lane);
+            } else {
+                const uint32_t so = (uint32_t)(st - lds);
+                return frag3_mn<BM / 8>(mnA[ks][0] + so, mnA[ks][1] + so, r0);
+            }
+        };
+        auto read_b = [&](const char *st, int ks, int j) -> u32x4 {
+            const int c0 = wn * WN + MI * j;
+            if constexpr (TB) {
+                if constexpr (MI == 16)
+                    return frag3_kc<BKS / 8>(st + A_BYTES, c0, 0, lane);
+                else
+                    return frag32_kc(st + A_BYTES, c0, ks, lane);
+            } else {
+                const uint32_t so = (uint32_t)(st - lds);
+                return frag3_mn<BN / 8>(mnB[ks][0] + so, mnB[ks][1] + so, c0);
+            }
+        };
+
+        using AccT = typename std::conditional<MI == 16, f32x4, f32x16>::type;
+        AccT acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = AccT{};
+
+        if (nst > 0) {
+            u32x4 fa[KS][FM], fb[KS][FN];   // one stage of fragments
+
+            // stages 0 .. S - 2 come first; stage b + S - 2 follows with stage b
+            const int pro = min(nst, S - 1);
+#pragma unroll
+            for (int t = 0; t < S - 1; ++t)
+                if (t < pro)
+                    issue(t);
+            wait_stage(0, pro - 1, true);
+            lds_barrier();
+
+            // load stage b into (fa, fb), after refilling the buffer of stage
+            // b - 2 with stage b + S - 2; the reads are left in flight
+            auto load = [&](int b) {
+                if (b >= 1 && b + S - 2 < nst)
+                    issue(b + S - 2);
+                const char *st = lds + (b % S) * STAGE;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        fb[ks][j] = read_b(st, ks, j);
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+                        fa[ks][i] = read_a(st, ks, i);
+                }
+            };
+            // multiply the stage in (fa, fb): 32 (16 x 16) or 16 (32 x 32) MFMAs
+            // with nothing to wait for
+            auto multiply = [&]() {
+                __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j) {
+                            // 16 x 16 blocks: the compiler's own MFMA, accumulators in
+                            // VGPRs (measured as fast as tied AGPR accumulators, with
+                            // no spills, and the compiler sees and covers every
+                            // hazard of a register it moves)
+                            if constexpr (MI == 16)
+                                mfma_chunk<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
+                            else
+                                mfma32_tied<Tr>(acc[i][j], fb[ks][j], fa[ks][i]);
+                        }
+                __builtin_amdgcn_s_setprio(0);
+            };
+            // before the barrier that opens phase 2b + 2 (stage b + 1 first read)
+            auto sync_next = [&](int b) {
+                if (b + 1 < nst)
+                    wait_stage(b + 1, min(nst - 1, b + S - 2), false);
+            };
+            // Each group runs its own straight-line loop (no role branches, so
+            // the accumulators stay in their AGPRs); both execute 2 nst + 1
+            // barriers, group 1 one phase behind group 0.
+            if (grp == 0) {
+                for (int b = 0; b < nst; ++b) {
+                    load(b);
+                    lds_barrier();
+                    multiply();
+                    sync_next(b);
+                    lds_barrier();
+                }
+                lds_barrier();
+            } else {
+                lds_barrier();
+                for (int b = 0; b < nst; ++b) {
+                    load(b);
+                    sync_next(b);
+                    lds_barrier();
+                    multiply();
+                    lds_barrier();
+                }
+            }
+            if constexpr (MI != 16)
+                mfma_drain();   // tied asm accumulators: the hazard the compiler cannot see
         }
+
+        // ---- epilogue: each lane holds runs of 4 consecutive columns of C
+        T *C = (T *)p.C;
+        float *W = p.ws + (int64_t)z * p.M * p.N;
+        auto store4 = [&](int m, int n, const f32x4 &v) {
+            if constexpr (SK) {
+                if (Wt) {   // the whole tile, rows and columns past M and N included
+                    *(f32x4 *)(Wt + (m - m0) * BN + (n - n0)) = v;
+                    return;
+                }
+            }
+            if (m >= p.M || n >= p.N)
+                return;
+            if (!SK && p.splits > 1) {
+                float *dst = W + (int64_t)m * p.N + n;
+                if (n + 3 < p.N && (p.N & 3) == 0) {
+                    *(f32x4 *)dst = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < p.N)
+                            dst[e] = v[e];
+                }
+                return;
+            }
+            store_out4<Tr>(C + (int64_t)m * p.ldc + n, v, p.N - n, p.c_vec && n + 3 < p.N, p.oe);
+        };
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (MI == 16) {
+                    // C[m0 + .. + (lane & 15)][n0 + .. + 4 (lane >> 4) .. + 3]
+                    store4(m0 + wm * WM + 16 * i + (lane & 15), n0 + wn * WN + 16 * j + 4 * (lane >> 4),
+                           acc[i][j]);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                         acc[i][j][4 * q + 3]};
+                        store4(m0 + wm * WM + 32 * i + (lane & 31),
+                               n0 + wn * WN + 32 * j + 8 * q + 4 * (lane >> 5), v);
+                    }
+                }
+            }
     };
 
     if constexpr (!SK) {
