@@ -45,6 +45,13 @@
  *
  * Errors: every entry point returns a tg_status; on failure nothing is
  * enqueued and tg_last_error() describes the cause (thread-local).
+ *
+ * Capture and threads: a call that needs no workspace, or is given one
+ * through tg_gemm_ex, only launches kernels on `stream`, so it can be
+ * recorded into a HIP graph (make one eager call first: it fills the
+ * library's per-device caches); its kernels sum in fixed orders, so replays
+ * reproduce the eager result bit for bit.  Calls from several host threads
+ * on their own streams are independent.
  */
 #ifndef TG_GEMM_H
 #define TG_GEMM_H
