@@ -226,6 +226,25 @@ def test_skinny(dtype, trans, shape):
         assert r["ok"], (split, r)
 
 
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("trans", [NN, NT])
+@pytest.mark.parametrize("shape", [(128, 128, 256), (200, 64, 264), (1000, 120, 1000), (136, 8, 512),
+                                   (584, 72, 1096), (4160, 128, 2048)])
+def test_skinny_tall_row_blocks(dtype, trans, shape):
+    """The 128-row block form (tile_m = 128): ragged last blocks (M not a
+    multiple of 128), every split, both B layouts, both output widths."""
+    import tiled_gemm_02_amd as tg
+    M, N, K = shape
+    _say("case skinny rb128", dtype, trans, shape)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=12)
+    for split in (1, 2, 4):
+        opts = dict(path=tg.TG_PATH_SKINNY, tile_m=128, split_k=split)
+        pl = tg.tg_gemm_plan(M, N, K, dtype, trans, opts)
+        assert pl["path"] == tg.TG_PATH_SKINNY and pl["tile_m"] == 128
+        r, _, _ = check_full(p, epilogue="leaky_relu" if split == 2 else None, options=opts)
+        assert r["ok"], (split, r)
+
+
 def test_skinny_integer_bitwise():
     import tiled_gemm_02_amd as tg
     p = make_int_problem(640, 128, 512, F16, NN, -2, 2, seed=3)

@@ -472,7 +472,8 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         kps = (kps + BK - 1) / BK * BK;
         a.kps = (int)kps;
         a.splits = pl.split_k;
-        a.nrb = (int)((p.M + kSkRows - 1) / kSkRows);
+        a.rb = pl.tile_m;
+        a.nrb = (int)((p.M + a.rb - 1) / a.rb);
         a.skew = kSkinnySkew;
         a.oe = oe;
         const int cb = elem_bytes(p.dtype);
@@ -751,8 +752,9 @@ int tg_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
             cands.push_back(tg_options{TG_PATH_MFMA, menu[i].bm, menu[i].bn, sp});
     cands.push_back(tg_options{TG_PATH_MFMA, 64, 64, 1});   // the element-wise tile
     cands.push_back(tg_options{TG_PATH_MFMA, 256, 256, TG_SPLIT_STREAM_K});
-    for (int sp : {1, 2, 4})
-        cands.push_back(tg_options{TG_PATH_SKINNY, 0, 0, sp});
+    for (int rb : {64, 128})
+        for (int sp : {1, 2, 4, 8})
+            cands.push_back(tg_options{TG_PATH_SKINNY, rb, 0, sp});
 
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t e0 = nullptr, e1 = nullptr;

@@ -49,13 +49,14 @@ struct SkinnyArgs {
     int M, N, K;
     int kps;         // K per split (multiple of kSkBK)
     int splits;
-    int nrb;         // row blocks, ceil(M / kSkRows)
+    int nrb;         // row blocks, ceil(M / rb)
+    int rb;          // rows per block: 64 or 128
     int skew;        // stages between the start points of consecutive XCDs
     OutEpi oe;       // output transform
     int c_vec;
 };
 
-constexpr int kSkRows = 64;     // C rows per workgroup
+constexpr int kSkRows = 64;     // C rows per workgroup (the default; 128 is also built)
 constexpr int kSkBK = 64;       // K per stage
 constexpr int kSkLds = 144 * 1024;   // LDS of the two rings
 constexpr int kSkStagesB = 4;        // B ring stages (A gets the rest)
@@ -100,7 +101,9 @@ __device__ __forceinline__ void sk_wait_younger(int y)
     }
 }
 
-template <typename Tr, bool TB, int CN>
+// RB: rows of C (and of A) per workgroup, 64 or 128.  Taller blocks read each
+// B stage for more rows: fewer of the CU's outstanding line requests go to B.
+template <typename Tr, bool TB, int CN, int RB = kSkRows>
 __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -108,8 +111,10 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
     constexpr int BK = kSkBK;
     constexpr int KS = BK / 32;                           // MFMA K steps per stage
     constexpr int WR = 2, WC = 2;                         // compute waves: a 2 x 2 grid
-    constexpr int MB = kSkRows / 16 / WR, NBK = CN / 16 / WC;   // 16 x 16 blocks per compute wave
-    constexpr int A_BYTES = kSkRows * BK * 2;             // 8 KiB: 8 copies of 1 KiB
+    static_assert(RB == 64 || RB == 128, "row block");
+    constexpr int MB = RB / 16 / WR, NBK = CN / 16 / WC;  // 16 x 16 blocks per compute wave
+    constexpr int A_BYTES = RB * BK * 2;                  // 8 or 16 KiB: copies of 1 KiB
+    constexpr int NAC = RB / 64;                          // A copies per A wave per stage
     constexpr int B_BYTES = CN * BK * 2;                  // 8 or 16 KiB
     constexpr int SB = kSkStagesB;                        // B ring
     constexpr int SA = (kSkLds - SB * B_BYTES) / A_BYTES; // A ring: the rest of LDS
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
     const int fr = lane & 15, fg = lane >> 4;
 
     const int rb = blockIdx.x;
-    const int row0 = rb * kSkRows;
+    const int row0 = rb * RB;
     const int z = blockIdx.y;
     const int kbeg = z * p.kps;
     const int kend = min(p.K, kbeg + p.kps);
@@ -147,24 +152,29 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
         return kbeg + ts * BK;
     };
 
-    // A copy (waves 8..15, one per stage): A rows 8c .. 8c + 7 (c = wave - 8),
-    // 128 bytes each; lane l stores chunk l % 8 of row 8c + l / 8, i.e. logical
-    // chunk (l % 8) ^ swz(row), into bytes [1024 c, + 1024) of the stage.
+    // A copy u of wave 8 + c (RB / 64 per stage): A rows 64 u + 8c .. + 7,
+    // 128 bytes each; lane l stores chunk l % 8 of row 64 u + 8c + l / 8, i.e.
+    // logical chunk (l % 8) ^ swz(row), into bytes [8192 u + 1024 c, + 1024)
+    // of the stage (row r at 128 r).
     // B copy u of wave w (0..7): copy j = w + 8 u of the stage's B tile.  Stored
     // N x K, like A (rows are columns); stored K x N, k-rows of BCH chunks, lane
     // l storing chunk l % BCH of k-row (64 / BCH) j + l / BCH.
     // Per lane: the byte offset at K offset 0 and the stage-relative K it reads.
-    uint32_t c_off[NBC];
-    int c_k[NBC];
+    constexpr int NC = NBC > NAC ? NBC : NAC;
+    uint32_t c_off[NC];
+    int c_k[NC];
     u32x4 rs;
     if (wave >= NBW) {
         const int c = wave - NBW;
-        const int rows_here = min(kSkRows, p.M - row0);
+        const int rows_here = min(RB, p.M - row0);
         rs = sk_rsrc(A + (int64_t)row0 * p.lda, (uint32_t)((int64_t)rows_here * p.lda * 2));
-        const int r = 8 * c + (lane >> 3);
-        const int lc = (lane & 7) ^ kc3_swz<8>(r);
-        c_k[0] = 8 * lc;
-        c_off[0] = (uint32_t)(r * p.lda * 2 + 16 * lc);
+#pragma unroll
+        for (int u = 0; u < NAC; ++u) {
+            const int r = 64 * u + 8 * c + (lane >> 3);
+            const int lc = (lane & 7) ^ kc3_swz<8>(r);
+            c_k[u] = 8 * lc;
+            c_off[u] = (uint32_t)(r * p.lda * 2 + 16 * lc);
+        }
     } else {
         rs = TB ? sk_rsrc(B, (uint32_t)((int64_t)p.N * p.ldb * 2)) : sk_rsrc(B, (uint32_t)((int64_t)p.K * p.ldb * 2));
 #pragma unroll
@@ -185,8 +195,11 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
     }
     auto issue_a = [&](int t) {
         const int k0 = stage_k0(t);
-        const uint32_t off = c_k[0] < kend - k0 ? c_off[0] + 2u * (uint32_t)k0 : kOut;
-        sk_copy(rs, off, lds_base + (uint32_t)((t % SA) * A_BYTES + (wave - NBW) * 1024));
+#pragma unroll
+        for (int u = 0; u < NAC; ++u) {
+            const uint32_t off = c_k[u] < kend - k0 ? c_off[u] + 2u * (uint32_t)k0 : kOut;
+            sk_copy(rs, off, lds_base + (uint32_t)((t % SA) * A_BYTES + u * 8192 + (wave - NBW) * 1024));
+        }
     };
     auto issue_b = [&](int t) {
         const int k0 = stage_k0(t);
@@ -228,7 +241,7 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs p)
             if (t < nst)
                 issue_a(t);
         for (int t = 0; t < nst; ++t) {
-            sk_wait_younger<1, SA - 2>(min(nst - 1, t + SA - 2) - t);
+            sk_wait_younger<NAC, SA - 2>(min(nst - 1, t + SA - 2) - t);
             lds_barrier();
             if (t + SA - 1 < nst)
                 issue_a(t + SA - 1);

@@ -423,7 +423,7 @@ static bool skinny_fits(const Problem &p)
     // 64-row block of A, and all of B, must span less than 2^31 bytes
     const int64_t lim = (int64_t)1 << 31;
     const bool tb = (p.trans & TG_TRANS_B) != 0;
-    const bool fit32 = (int64_t)kSkinnyRows * p.lda * 2 < lim && (tb ? p.N : p.K) * p.ldb * 2 < lim;
+    const bool fit32 = (int64_t)kSkinnyMaxRows * p.lda * 2 < lim && (tb ? p.N : p.K) * p.ldb * 2 < lim;
     return p.dtype != TG_F32 && p.N <= kSkinnyMaxN && p.N >= 8 && p.M >= 2 * kSkinnyRows &&
            vec_ok(p) && !(p.trans & TG_TRANS_A) && fit32;
 }
@@ -442,7 +442,19 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
         return TG_ERR_UNSUPPORTED;
     }
     const int BK = kSkinnyBK;
-    const int64_t tm = (p.M + kSkinnyRows - 1) / kSkinnyRows;
+    // 128-row blocks read each B stage for twice the rows, so fewer of the
+    // CU's outstanding requests go to B; measured on MI355X with 128-wide
+    // outputs: 8192 x 128 x 8192 +9 %, 16384 x 128 x 8192 +8 %, but
+    // 8192 x 128 x 16384 -15 % (rows of 32 KiB); 64-wide outputs: no change
+    int rb = (p.N > 64 && p.K <= 8192 && p.M >= 2 * kSkinnyMaxRows) ? kSkinnyMaxRows : kSkinnyRows;
+    if (opts && opts->tile_m > 0) {
+        if (opts->tile_m != 64 && opts->tile_m != 128) {
+            *why = "skinny row blocks are 64 or 128 rows";
+            return TG_ERR_UNSUPPORTED;
+        }
+        rb = opts->tile_m;
+    }
+    const int64_t tm = (p.M + rb - 1) / rb;
     // split K until every CU streams its own part of A, four stages per split at least
     int s = 1;
     if (opts && opts->split_k > 0) {
@@ -455,7 +467,7 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
     kps = (kps + BK - 1) / BK * BK;
     s = (int)((p.K + kps - 1) / kps);
     out->path = TG_PATH_SKINNY;
-    out->tile_m = kSkinnyRows;
+    out->tile_m = rb;
     out->tile_n = p.N > 64 ? 128 : 64;
     out->tile_k = BK;
     out->split_k = s;
@@ -465,7 +477,7 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
     out->workgroups = tm * s;
     const int64_t slots = (int64_t)chip.num_cus * out->occupancy;
     out->waves = (out->workgroups + slots - 1) / slots;
-    out->tile_eff = (double)p.N / out->tile_n * (double)p.M / (tm * kSkinnyRows);
+    out->tile_eff = (double)p.N / out->tile_n * (double)p.M / (tm * rb);
     out->wave_eff = (double)out->workgroups / (double)(out->waves * slots);
     out->workspace_bytes = s > 1 ? (uint64_t)s * p.M * p.N * 4u : 0;
     const double bytes = alg_bytes(p) + 2.0 * (double)out->workspace_bytes;

@@ -49,7 +49,8 @@ int model_occupancy(int dtype, int bm, int bn, bool vec);
 
 // Skinny kernel geometry (N <= kSkinnyMaxN): a workgroup covers 64 rows and
 // all columns (64 or 128); K is split until the row blocks fill the CUs.
-constexpr int kSkinnyRows = 64;        // output rows per workgroup
+constexpr int kSkinnyRows = 64;        // output rows per workgroup (default)
+constexpr int kSkinnyMaxRows = 128;    // the taller row block the kernel also offers
 constexpr int kSkinnyMaxN = 128;       // widest output it covers in one pass
 constexpr int kSkinnyBK = 64;          // K per pipeline stage, the granularity of a split
 constexpr int kSkinnySkew = 16;        // stages between the K start points of consecutive XCDs
