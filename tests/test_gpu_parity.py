@@ -137,14 +137,16 @@ def test_leaky_relu_epilogue(dtype, trans):
 
 # ---------------------------------------------------------------- forced plans
 
-def _tiles(dtype):
-    return [(128, 128), (64, 64)] if dtype == F32 else [(256, 256), (256, 128), (128, 128), (128, 64), (64, 64)]
+def _tiles(dtype, trans):
+    if dtype == F32:   # the float32 256 x 256 kernel takes K-contiguous A and B only
+        return ([(256, 256)] if trans == NT else []) + [(128, 128), (64, 64)]
+    return [(256, 256), (256, 128), (128, 128), (128, 64), (64, 64)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("trans", [NN, NT])
 def test_every_tile(dtype, trans):
-    for tm, tn in _tiles(dtype):
+    for tm, tn in _tiles(dtype, trans):
         _say("case tile", dtype, trans, tm, tn)
         p = make_problem(296, 280, 136, dtype, trans, "normal", seed=6)
         r, _, _ = check_full(p, options=dict(tile_m=tm, tile_n=tn, split_k=1))
@@ -156,6 +158,47 @@ def test_every_tile(dtype, trans):
     assert r["ok"], r
     with pytest.raises(tg.TgError):
         run_gpu(p, options=dict(tile_m=128, tile_n=128))
+    if dtype == F32 and trans != NT:
+        p = make_problem(296, 280, 136, dtype, trans, "normal", seed=6)
+        with pytest.raises(tg.TgError):
+            run_gpu(p, options=dict(tile_m=256, tile_n=256))
+
+
+# float32 on the 256 x 256 ping-pong kernel: ragged M and N edges, a K tail
+# (K % 16 != 0: the partial stage goes through registers), K splits, the
+# epilogue and alpha / beta
+F32_PP_CASES = [
+    (300, 520, 1000, 1, None, 1.0, 0.0),
+    (256, 256, 16, 1, None, 1.0, 0.0),
+    (520, 264, 4, 1, None, 1.0, 0.0),
+    (516, 772, 1204, 3, None, 1.0, 0.0),
+    (264, 300, 2000, 2, "leaky_relu", 0.5, -1.5),
+]
+
+
+@pytest.mark.parametrize("case", F32_PP_CASES, ids=lambda c: "x".join(map(str, c[:4])))
+def test_f32_pingpong(case):
+    M, N, K, split, epi, alpha, beta = case
+    _say("case f32 pingpong", case)
+    p = make_problem(M, N, K, F32, NT, "normal", seed=21)
+    opts = dict(tile_m=256, tile_n=256, split_k=split)
+    if alpha == 1.0 and beta == 0.0:
+        r, _, _ = check_full(p, epilogue=epi, options=opts)
+    else:
+        r, _, _ = check_scaled(p, alpha, beta, epilogue=epi, options=opts)
+    assert r["ok"], (case, r)
+
+
+def test_f32_pingpong_is_planned_and_sampled():
+    """A large float32 NT product plans the 256 x 256 tile; sampled outputs
+    against the oracle."""
+    import tiled_gemm_02_amd as tg
+    p = make_problem(4096, 4096, 4096, F32, NT, "normal", seed=0)
+    pl = tg.tg_gemm_plan(p.M, p.N, p.K, tg.TG_F32, tg.TG_NT)
+    assert (pl["tile_m"], pl["tile_n"]) == (256, 256), pl
+    _say("case f32 4096 nt sampled")
+    r = check_sampled(p, n=2048)
+    assert r["ok"], r
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

@@ -176,3 +176,16 @@ def test_stream_k_plans():
             tg.tg_plan_model(*args, tg.TG_NN, options=opts)
     with pytest.raises(tg.TgError):
         tg.tg_plan_model(1024, 1024, 4096, F, tg.TG_NN, options=dict(split_k=-2))
+
+
+def test_f32_tiles():
+    """float32: the 256 x 256 tile (ping-pong kernel) only for K-contiguous A
+    and B (NT) with leading dimensions up to 2^21; 128 x 128 otherwise."""
+    F = tg.TG_F32
+    p = tg.tg_plan_model(8192, 8192, 8192, F, tg.TG_NT)
+    assert (p["tile_m"], p["tile_n"], p["tiles"]) == (256, 256, 1024)
+    for tr in (tg.TG_NN, tg.TG_TN, tg.TG_TT):
+        p = tg.tg_plan_model(8192, 8192, 8192, F, tr)
+        assert (p["tile_m"], p["tile_n"]) == (128, 128)
+    p = tg.tg_plan_model(1024, 1024, 1024, F, tg.TG_NT, options=dict(tile_m=256, tile_n=256))
+    assert p["tile_m"] == 256

@@ -45,6 +45,7 @@ hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a,
     switch (dtype) {
     case TG_F16: return launch_mfma2_f16(trans, bm, bn, a, s);
     case TG_BF16: return launch_mfma2_bf16(trans, bm, bn, a, s);
+    case TG_F32: return launch_mfma2_f32(trans, bm, bn, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -54,6 +55,7 @@ int mfma2_occupancy(int dtype, int trans, int bm, int bn)
     switch (dtype) {
     case TG_F16: return mfma2_occupancy_f16(trans, bm, bn);
     case TG_BF16: return mfma2_occupancy_bf16(trans, bm, bn);
+    case TG_F32: return mfma2_occupancy_f32(trans, bm, bn);
     }
     return 0;
 }
@@ -73,13 +75,16 @@ static int mfma_variant()
 // The LDS-DMA kernel addresses each lane's copy with a 32-bit byte offset from
 // a per-tile 64-bit base: at most 256 rows (or 64 K-rows) of one operand, so a
 // leading dimension up to 2^22 elements keeps every offset below 2^31.
-static bool use_mfma2(int dtype, int trans, bool vec, int64_t M, int64_t N, int64_t K, int64_t lda,
-                      int64_t ldb)
+// float32: only the 256 x 256 tile, with K-contiguous A and B, has such a kernel
+// (its leading dimensions count 16-bit units: at most 2^21 float32 elements).
+static bool use_mfma2(int dtype, int trans, bool vec, int bm, int bn, int64_t lda, int64_t ldb)
 {
-    (void)trans; (void)M; (void)N; (void)K;
-    if (dtype == TG_F32 || !vec || mfma_variant() != 2)
+    const int64_t lim = (int64_t(1) << 23) / elem_bytes(dtype);
+    if (!vec || lda > lim || ldb > lim)
         return false;
-    return lda <= (int64_t(1) << 22) && ldb <= (int64_t(1) << 22);
+    if (dtype == TG_F32)
+        return bm == 256 && bn == 256 && trans == TG_NT;
+    return mfma_variant() == 2;
 }
 
 int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec)
@@ -308,8 +313,8 @@ static int device_occ(int dtype, int trans, int bm, int bn, bool vec, void *ctx)
     std::lock_guard<std::mutex> lk(g_dev_mu);
     int &slot = d->occ[dtype][trans][ts][vec ? 1 : 0];
     if (slot == 0) {
-        int n = (dtype != TG_F32 && vec && mfma_variant() == 2) ? mfma2_occupancy(dtype, trans, bm, bn)
-                                                                  : mfma_occupancy(dtype, trans, bm, bn, vec);
+        int n = use_mfma2(dtype, trans, vec, bm, bn, 0, 0) ? mfma2_occupancy(dtype, trans, bm, bn)
+                                                           : mfma_occupancy(dtype, trans, bm, bn, vec);
         slot = n > 0 ? n : -1;
     }
     return slot > 0 ? slot : model_occupancy(dtype, bm, bn, vec);
@@ -448,7 +453,7 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         kps = (kps + BK - 1) / BK * BK;
         a.kps = (int)kps;
         a.splits = pl.split_k;
-        if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, p.M, p.N, p.K, p.lda, p.ldb))
+        if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, pl.tile_m, pl.tile_n, p.lda, p.ldb))
             e = launch_mfma2(p.dtype, p.trans, pl.tile_m, pl.tile_n, a, s);
         else
             e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);

@@ -1,5 +1,8 @@
-// mfma_pingpong.hpp -- 256 x 256 macro-tile GEMM for 16-bit operands with two
-// wave groups that alternate between loading and multiplying.
+// mfma_pingpong.hpp -- 256 x 256 macro-tile GEMM with two wave groups that
+// alternate between loading and multiplying: 16-bit operands in every layout,
+// and float32 operands when A and B are both K-contiguous (a float32 value is
+// copied as two 16-bit units, so a stage row holds 16 values of K and a phase
+// is 128 v_mfma_f32_16x16x4f32 per wave).
 //
 // Tiling ("Matrix Multiplication Background User's Guide", section 2.1): one
 // 256 x 256 tile of C per workgroup, eight wave64s in a 2 x 4 grid, each wave
@@ -99,6 +102,11 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
     constexpr int NDMA = OpA::PER_WAVE;                  // copies per wave per stage
     static_assert(OpA::PER_WAVE == OpB::PER_WAVE, "both groups copy the same amount");
     static_assert(S >= 3 && S <= 5 && (S - 2) * NDMA < 64, "stage count");
+    // float32 operands are copied as pairs of 16-bit units: a stage row is
+    // then 16 values of K, and only K-contiguous operands are supported (the
+    // transposed LDS reads of the M/N-contiguous layouts are 16-bit reads)
+    constexpr int EW = Tr::kBytes / 2;
+    static_assert(EW == 1 || (!TA && TB && !SK && MI == 16), "float32: K-contiguous A and B only");
 
     __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
 
@@ -116,16 +124,17 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
     // its last barrier.
     auto item = [&](const int m0, const int n0, const int z, const int kbeg, const int klen,
                     float *const Wt) {
-        const int nfull = klen / BKS;
-        const int has_tail = (klen % BKS) != 0;
+        // K in 16-bit units from here on (float32: twice the element count)
+        const int nfull = klen * EW / BKS;
+        const int has_tail = (klen * EW % BKS) != 0;
         const int nst = nfull + has_tail;
 
         OpA oa;
         OpB ob;
         if (grp == 0)
-            oa.init((const uint16_t *)p.A, p.lda, p.rows_a, m0, kbeg, gwave, lane);
+            oa.init((const uint16_t *)p.A, p.lda * EW, p.rows_a, m0, kbeg * EW, gwave, lane);
         else
-            ob.init((const uint16_t *)p.B, p.ldb, p.cols_b, n0, kbeg, gwave, lane);
+            ob.init((const uint16_t *)p.B, p.ldb * EW, p.cols_b, n0, kbeg * EW, gwave, lane);
         const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
         // this group's operand of processing stage t into its buffer: the K tail
         // (stage 0 when there is one) through registers, the rest by DMA
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
             const int slot = t % S;
             if (has_tail && t == 0) {
                 char *st = lds + slot * STAGE;
-                const int krel = klen - nfull * BKS;
+                const int krel = klen * EW - nfull * BKS;
                 if (grp == 0)
                     oa.tail(nfull, krel, st, gwave, lane);
                 else
@@ -248,9 +257,23 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
                 }
             };
             // multiply the stage in (fa, fb): 32 (16 x 16) or 16 (32 x 32) MFMAs
-            // with nothing to wait for
+            // with nothing to wait for (float32: 128 v_mfma_f32_16x16x4f32,
+            // element e of every fragment chunk at a time, so that no MFMA
+            // waits for the one before it)
             auto multiply = [&]() {
                 __builtin_amdgcn_s_setprio(2);
+                if constexpr (EW == 2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < FN; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    u32_as_f32(fb[0][j][e]), u32_as_f32(fa[0][i][e]), acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_s_setprio(0);
+                    return;
+                }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
 #pragma unroll

@@ -33,9 +33,14 @@ static const TileSpec kTiles16[] = {
     {256, 256, 0.50, 160}, {256, 128, 0.355, 96}, {128, 128, 0.385, 64},
     {128, 64, 0.31, 48},   {64, 64, 0.22, 32},
 };
+// float32: 256 x 256 is the ping-pong kernel, K-contiguous A and B only
+// (tile_fits); the smaller tiles are the register-staged kernel.  Measured at
+// 8192^3 on MI355X: 137.6 TFLOP/s (NT, 256 x 256) and 126 (NN, 128 x 128) of
+// the 157.3 TFLOP/s float32 matrix peak.
 static const TileSpec kTiles32[] = {
-    {128, 128, 1.00, 64},
-    {64, 64, 0.60, 32},
+    {256, 256, 0.87, 160},
+    {128, 128, 0.80, 64},
+    {64, 64, 0.48, 32},
 };
 
 int tile_menu(int dtype, const TileSpec **out)
@@ -58,6 +63,14 @@ bool has_mfma_tile(int dtype, int bm, int bn, bool vec)
         if (t[i].bm == bm && t[i].bn == bn)
             return true;
     return false;
+}
+
+// Whether the kernel behind a menu tile takes this problem's layout.
+static bool tile_fits(const Problem &p, int bm, int bn)
+{
+    if (p.dtype == TG_F32 && bm == 256 && bn == 256)
+        return p.trans == TG_NT && p.lda <= (1 << 21) && p.ldb <= (1 << 21);
+    return true;
 }
 
 static const TileSpec *find_tile(int dtype, int bm, int bn)
@@ -319,6 +332,8 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
             return TG_ERR_ARG;
         }
         const TileSpec *f = vec ? find_tile(p.dtype, opts->tile_m, opts->tile_n) : nullptr;
+        if (f && !tile_fits(p, f->bm, f->bn))
+            f = nullptr;
         if (!vec && opts->tile_m == 64 && opts->tile_n == 64)
             f = &generic;
         if (!f) {
@@ -369,6 +384,8 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
     }
     for (int i = 0; i < nmenu && !force_sk; ++i) {
         const TileSpec &ts = menu[i];
+        if (!tile_fits(p, ts.bm, ts.bn))
+            continue;
         int occ = occupancy > 0 ? occupancy
                                 : (occ_fn ? occ_fn(p.dtype, p.trans, ts.bm, ts.bn, vec, occ_ctx)
                                           : model_occupancy(p.dtype, ts.bm, ts.bn, vec));
