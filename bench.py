@@ -491,7 +491,7 @@ def align_sweep(out_path: str, reps: int = 5):
             ts.append(e0.elapsed_time(e1))
         ms = sorted(ts)[len(ts) // 2]
         tf = 2.0 * M * N * K / ms / 1e9
-        loads = {0: "element-wise", 1: "vector", 2: "copied"}[pl["vector_io"]]
+        loads = {0: "element-wise", 1: "vector", 2: "copied", 3: "copied as NT"}[pl["vector_io"]]
         # plan_for assumes packed operands; the real call sees the same strides here
         lines.append(f"| {M} | {N} | {K} | {pl['path_name']} | {pl['tile_m']}x{pl['tile_n']} | "
                      f"{pl['split_k']} | {loads} | {ms * 1e3:.0f} | {tf:.0f} |")

@@ -139,7 +139,11 @@ typedef struct tg_plan {
     int32_t num_cus;     /* compute units the wave model used */
     int32_t vector_io;   /* 1 = 128-bit operand loads, 0 = element-wise, 2 = A and B first
                             copied into zero-padded 16-byte-aligned buffers at the start of
-                            the workspace (K rounded up to 16 bytes), then 128-bit loads */
+                            the workspace (K rounded up to 16 bytes), then 128-bit loads;
+                            3 (float32) = the same copies laid out K-contiguous (A as M x K,
+                            B as N x K, transposing operands stored the other way; when the
+                            operands are aligned only those are copied) and the product
+                            run as TG_NT */
     int64_t tiles;       /* ceil(M/tile_m) * ceil(N/tile_n) */
     int64_t workgroups;  /* tiles * split_k (MFMA/skinny), the stream-K workgroups, or the GEMV grid */
     int64_t waves;       /* ceil(workgroups / (num_cus * occupancy)) */

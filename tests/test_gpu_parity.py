@@ -189,16 +189,47 @@ def test_f32_pingpong(case):
     assert r["ok"], (case, r)
 
 
+# float32 in the other layouts through K-contiguous copies (vector_io 3): the
+# operands stored M/N-contiguous are transposed into the workspace, the NT
+# product runs on the 256 x 256 kernel; unaligned sizes copy and pad both
+F32_NT_COPY_CASES = [
+    (520, 1000, 1028, NN, 1.0, 0.0, None),
+    (520, 1000, 1028, TN, 1.0, 0.0, None),
+    (520, 1000, 1028, TT, 1.0, 0.0, None),
+    (517, 1001, 1027, NN, 1.0, 0.0, None),
+    (517, 1001, 1027, TT, 1.0, 0.0, None),
+    (600, 904, 1100, TN, -0.5, 2.0, "leaky_relu"),
+]
+
+
+@pytest.mark.parametrize("case", F32_NT_COPY_CASES,
+                         ids=lambda c: "x".join(map(str, c[:3])) + f"-t{c[3]}")
+def test_f32_nt_copies(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, trans, alpha, beta, epi = case
+    _say("case f32 nt copies", case)
+    opts = dict(tile_m=256, tile_n=256, split_k=1)
+    pl = tg.tg_gemm_plan(M, N, K, tg.TG_F32, trans, options=opts)
+    assert pl["vector_io"] == 3 and pl["tile_m"] == 256, pl
+    p = make_problem(M, N, K, F32, trans, "normal", seed=23)
+    if alpha == 1.0 and beta == 0.0:
+        r, _, _ = check_full(p, epilogue=epi, options=opts)
+    else:
+        r, _, _ = check_scaled(p, alpha, beta, epilogue=epi, options=opts)
+    assert r["ok"], (case, r)
+
+
 def test_f32_pingpong_is_planned_and_sampled():
     """A large float32 NT product plans the 256 x 256 tile; sampled outputs
     against the oracle."""
     import tiled_gemm_02_amd as tg
-    p = make_problem(4096, 4096, 4096, F32, NT, "normal", seed=0)
-    pl = tg.tg_gemm_plan(p.M, p.N, p.K, tg.TG_F32, tg.TG_NT)
-    assert (pl["tile_m"], pl["tile_n"]) == (256, 256), pl
-    _say("case f32 4096 nt sampled")
-    r = check_sampled(p, n=2048)
-    assert r["ok"], r
+    for trans, vio in [(NT, 1), (NN, 3)]:
+        p = make_problem(4096, 4096, 4096, F32, trans, "normal", seed=0)
+        pl = tg.tg_gemm_plan(p.M, p.N, p.K, tg.TG_F32, trans)
+        assert (pl["tile_m"], pl["tile_n"], pl["vector_io"]) == (256, 256, vio), pl
+        _say("case f32 4096 sampled", trans)
+        r = check_sampled(p, n=2048)
+        assert r["ok"], r
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

@@ -183,9 +183,36 @@ def test_f32_tiles():
     and B (NT) with leading dimensions up to 2^21; 128 x 128 otherwise."""
     F = tg.TG_F32
     p = tg.tg_plan_model(8192, 8192, 8192, F, tg.TG_NT)
-    assert (p["tile_m"], p["tile_n"], p["tiles"]) == (256, 256, 1024)
-    for tr in (tg.TG_NN, tg.TG_TN, tg.TG_TT):
-        p = tg.tg_plan_model(8192, 8192, 8192, F, tr)
-        assert (p["tile_m"], p["tile_n"]) == (128, 128)
+    assert (p["tile_m"], p["tile_n"], p["tiles"], p["vector_io"]) == (256, 256, 1024, 1)
     p = tg.tg_plan_model(1024, 1024, 1024, F, tg.TG_NT, options=dict(tile_m=256, tile_n=256))
     assert p["tile_m"] == 256
+    # the other layouts without copies: the register-staged 128 x 128 kernel
+    for tr in (tg.TG_NN, tg.TG_TN, tg.TG_TT):
+        p = tg.tg_plan_model(8192, 8192, 8192, F, tr, options=dict(tile_m=128, tile_n=128, split_k=1))
+        assert (p["tile_m"], p["tile_n"], p["vector_io"]) == (128, 128, 1)
+
+
+def test_f32_nt_copies():
+    """Large float32 products stored in another layout copy the operands that
+    are M/N-contiguous into K-contiguous buffers (transposing them) and run
+    the NT product on the 256 x 256 kernel (vector_io 3); aligned operands
+    already K-contiguous are read in place; small products stay direct."""
+    F = tg.TG_F32
+    n = 8192
+    plane = n * n * 4
+    for tr, copied in [(tg.TG_NN, 1), (tg.TG_TN, 2), (tg.TG_TT, 1)]:
+        p = tg.tg_plan_model(n, n, n, F, tr)
+        assert (p["tile_m"], p["tile_n"], p["vector_io"]) == (256, 256, 3), (tr, p)
+        assert p["workspace_bytes"] == copied * plane
+        # the copies are priced: the plan costs more than the NT product alone
+        assert p["pred_us"] > tg.tg_plan_model(n, n, n, F, tg.TG_NT)["pred_us"]
+    assert tg.tg_plan_model(1024, 1024, 1024, F, tg.TG_NN)["vector_io"] == 1
+    assert tg.tg_plan_model(300, 200, 100, F, tg.TG_NN)["vector_io"] == 1
+    # unaligned float32: both operands copied, padded, laid out for NT
+    p = tg.tg_plan_model(4097, 4095, 4099, F, tg.TG_NN)
+    assert p["vector_io"] == 3
+    kp, mp, np_ = 4100, 4100, 4096
+    assert p["workspace_bytes"] >= round256(mp * kp * 4) + round256(np_ * kp * 4)
+    # 16-bit products never take the NT copies
+    assert tg.tg_plan_model(n, n, n, tg.TG_F16, tg.TG_NN)["vector_io"] == 1
+    assert tg.tg_plan_model(4097, 4095, 4099, tg.TG_F16, tg.TG_NN)["vector_io"] == 2

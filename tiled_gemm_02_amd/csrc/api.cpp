@@ -110,8 +110,16 @@ hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int64_t 
 }
 
 hipError_t launch_pack(int dtype, const void *src, int64_t lds, int64_t rows, int64_t cols, void *dst,
-                       int64_t drows, int64_t dcols, hipStream_t s)
+                       int64_t drows, int64_t dcols, hipStream_t s, bool transposed)
 {
+    if (transposed) {
+        switch (dtype) {
+        case TG_F16: return launch_pack_t_f16(src, lds, rows, cols, dst, drows, dcols, s);
+        case TG_BF16: return launch_pack_t_bf16(src, lds, rows, cols, dst, drows, dcols, s);
+        case TG_F32: return launch_pack_t_f32(src, lds, rows, cols, dst, drows, dcols, s);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (dtype) {
     case TG_F16: return launch_pack_f16(src, lds, rows, cols, dst, drows, dcols, s);
     case TG_BF16: return launch_pack_bf16(src, lds, rows, cols, dst, drows, dcols, s);
@@ -606,17 +614,23 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
             }
         }
     }
-    if (pl.vector_io == 2) {
-        // copy A and B into zero-padded aligned buffers, then run the aligned plan
-        const PackLayout L = pack_layout(p);
-        const Problem q = packed_problem(p);
+    if (pl.vector_io == 2 || pl.vector_io == 3) {
+        // copy A and B into zero-padded aligned buffers (3: laid out for the NT
+        // product, transposing where needed), then run the aligned plan
+        const bool nt = pl.vector_io == 3;
+        const PackLayout L = pack_layout(p, nt);
+        const Problem q = packed_problem(p, nt);
         const bool ta = trans & TG_TRANS_A, tb = trans & TG_TRANS_B;
         char *w = (char *)ws;
-        hipError_t e = launch_pack(dtype, A, lda, ta ? K : M, ta ? M : K, w + L.a_off, L.a_rows,
-                                   L.a_cols, s);
-        if (e == hipSuccess)
-            e = launch_pack(dtype, B, ldb, tb ? N : K, tb ? K : N, w + L.b_off, L.b_rows, L.b_cols,
-                            s);
+        const void *Ap = L.a_copy ? (const void *)(w + L.a_off) : A;
+        const void *Bp = L.b_copy ? (const void *)(w + L.b_off) : B;
+        hipError_t e = hipSuccess;
+        if (L.a_copy)
+            e = launch_pack(dtype, A, lda, ta ? K : M, ta ? M : K, w + L.a_off, L.a_rows, L.a_cols, s,
+                            L.a_trans);
+        if (e == hipSuccess && L.b_copy)
+            e = launch_pack(dtype, B, ldb, tb ? N : K, tb ? K : N, w + L.b_off, L.b_rows, L.b_cols, s,
+                            L.b_trans);
         if (e != hipSuccess) {
             if (own_ws)
                 (void)hipFreeAsync(ws, s);
@@ -630,7 +644,7 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
         Problem r = q;
         r.M = M;
         r.N = N;
-        rc = run_plan(inner, r, w + L.a_off, w + L.b_off, C, epi, w + L.bytes, s, q.M, q.N);
+        rc = run_plan(inner, r, Ap, Bp, C, epi, w + L.bytes, s, q.M, q.N);
         if (own_ws)
             (void)hipFreeAsync(ws, s);
         if (rc != TG_OK)

@@ -107,4 +107,58 @@ __global__ __launch_bounds__(256) void pack_kernel(const void *src_, int64_t lds
     }
 }
 
+// Transposing aligned copy of one operand: dst (drows x dcols, row-major,
+// ld = dcols, a multiple of 16 bytes) gets the transpose of src (rows x cols,
+// ld = lds): dst[i][j] = src[j][i] for i < cols, j < rows, zeros elsewhere.
+// A workgroup moves one 64 x 64 block of dst through LDS (rows padded by one
+// element so the column reads spread over the banks): it reads the block's
+// source rows along their contiguous dimension and writes dst rows four
+// elements per thread.
+template <typename Tr>
+__global__ __launch_bounds__(256) void pack_t_kernel(const void *src_, int64_t lds, int64_t rows,
+                                                     int64_t cols, void *dst_, int64_t drows,
+                                                     int64_t dcols)
+{
+    using W = std::conditional_t<Tr::kBytes == 2, uint16_t, uint32_t>;
+    typedef W w4 __attribute__((ext_vector_type(4)));
+    __shared__ W t[64][65];
+    const W *src = (const W *)src_;
+    W *dst = (W *)dst_;
+    const int64_t bcols = (dcols + 63) / 64;
+    const int64_t i0 = (int64_t)(blockIdx.x / bcols) * 64;   // dst rows = src columns
+    const int64_t j0 = (int64_t)(blockIdx.x % bcols) * 64;   // dst columns = src rows
+    const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
+    const bool vec = ((uintptr_t)src_ % sizeof(w4)) == 0 && (lds & 3) == 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = tr + 16 * q;          // source row j0 + r, columns i0 + tc .. + 3
+        const int64_t sr = j0 + r;
+        if (vec && sr < rows && i0 + tc + 3 < cols) {
+            const w4 v = *(const w4 *)(src + sr * lds + i0 + tc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                t[r][tc + e] = v[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t sc = i0 + tc + e;
+                t[r][tc + e] = (sr < rows && sc < cols) ? src[sr * lds + sc] : (W)0;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = tr + 16 * q;          // dst row i0 + r, columns j0 + tc .. + 3
+        const int64_t di = i0 + r, dj = j0 + tc;
+        if (di < drows && dj < dcols) {
+            w4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = t[tc + e][r];
+            *(w4 *)(dst + di * dcols + dj) = v;
+        }
+    }
+}
+
 }  // namespace tg

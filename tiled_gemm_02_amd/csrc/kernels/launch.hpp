@@ -28,8 +28,9 @@ hipError_t launch_splitk_reduce(int dtype, const float *ws, int splits, int64_t 
                                 int M, int N, void *C, int64_t ldc, const OutEpi &oe, int c_vec,
                                 hipStream_t s);
 // Aligned, zero-padded copy of a rows x cols operand into drows x dcols.
+// transposed: dst (drows x dcols) gets the transpose of src (rows x cols) instead.
 hipError_t launch_pack(int dtype, const void *src, int64_t lds, int64_t rows, int64_t cols, void *dst,
-                       int64_t drows, int64_t dcols, hipStream_t s);
+                       int64_t drows, int64_t dcols, hipStream_t s, bool transposed = false);
 // C = epi(beta * C): K == 0 or alpha == 0.
 hipError_t launch_scale_c(int dtype, void *C, int M, int N, int64_t ldc, const OutEpi &oe,
                           hipStream_t s);
@@ -52,6 +53,8 @@ hipError_t launch_softmax(int dtype, int q, int c, bool vec, const SoftmaxArgs &
                                            OutEpi oe, int c_vec, hipStream_t s);                 \
     hipError_t launch_pack_##NAME(const void *src, int64_t lds, int64_t rows, int64_t cols,      \
                                   void *dst, int64_t drows, int64_t dcols, hipStream_t s);       \
+    hipError_t launch_pack_t_##NAME(const void *src, int64_t lds, int64_t rows, int64_t cols,    \
+                                    void *dst, int64_t drows, int64_t dcols, hipStream_t s);     \
     hipError_t launch_scale_c_##NAME(void *C, int M, int N, int64_t ldc, OutEpi oe,             \
                                      hipStream_t s);                                             \
     hipError_t launch_gemv_##NAME(bool rows_form, bool vec, int lpr, const GemvArgs &a,          \

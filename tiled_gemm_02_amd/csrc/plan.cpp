@@ -535,32 +535,61 @@ void softmax_shape(int dtype, int64_t N, int *q, int *c)
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-Problem packed_problem(const Problem &p)
+Problem packed_problem(const Problem &p, bool nt)
 {
     const int E = chunk_elems(p.dtype);
     Problem q = p;
+    if (nt && vec_ok(p)) {
+        // aligned: only the operands stored the other way are copied
+        q.trans = TG_NT;
+        if (p.trans & TG_TRANS_A)
+            q.lda = p.K;
+        if (!(p.trans & TG_TRANS_B))
+            q.ldb = p.K;
+        return q;
+    }
     q.M = round_up(p.M, E);
     q.N = round_up(p.N, E);
     q.K = round_up(p.K, E);
-    q.lda = (p.trans & TG_TRANS_A) ? q.M : q.K;
-    q.ldb = (p.trans & TG_TRANS_B) ? q.K : q.N;
+    if (nt) {
+        q.trans = TG_NT;
+        q.lda = q.K;
+        q.ldb = q.K;
+    } else {
+        q.lda = (p.trans & TG_TRANS_A) ? q.M : q.K;
+        q.ldb = (p.trans & TG_TRANS_B) ? q.K : q.N;
+    }
     q.ptrs_aligned = true;
     return q;
 }
 
-PackLayout pack_layout(const Problem &p)
+PackLayout pack_layout(const Problem &p, bool nt)
 {
-    const Problem q = packed_problem(p);
+    const Problem q = packed_problem(p, nt);
     const int64_t es = elem_bytes(p.dtype);
     PackLayout L;
     const bool ta = p.trans & TG_TRANS_A, tb = p.trans & TG_TRANS_B;
-    L.a_rows = ta ? q.K : q.M;
-    L.a_cols = ta ? q.M : q.K;
-    L.b_rows = tb ? q.N : q.K;
-    L.b_cols = tb ? q.K : q.N;
+    if (nt) {
+        const bool all = !vec_ok(p);
+        L.a_copy = all || ta;
+        L.b_copy = all || !tb;
+        L.a_trans = ta;
+        L.b_trans = !tb;
+        L.a_rows = q.M;
+        L.a_cols = q.K;
+        L.b_rows = q.N;
+        L.b_cols = q.K;
+    } else {
+        L.a_copy = L.b_copy = true;
+        L.a_trans = L.b_trans = false;
+        L.a_rows = ta ? q.K : q.M;
+        L.a_cols = ta ? q.M : q.K;
+        L.b_rows = tb ? q.N : q.K;
+        L.b_cols = tb ? q.K : q.N;
+    }
     L.a_off = 0;
-    L.b_off = (uint64_t)round_up(L.a_rows * L.a_cols * es, 256);
-    L.bytes = L.b_off + (uint64_t)round_up(L.b_rows * L.b_cols * es, 256);
+    L.b_off = L.a_copy ? (uint64_t)round_up(L.a_rows * L.a_cols * es, 256) : 0;
+    L.bytes = L.b_off + (L.b_copy ? (uint64_t)round_up(L.b_rows * L.b_cols * es, 256) : 0);
     L.padded_mn = q.M != p.M || q.N != p.N;
     return L;
 }
@@ -568,6 +597,10 @@ PackLayout pack_layout(const Problem &p)
 // Worth copying: the element-wise kernel runs at a few percent of the vector
 // ones, so above about 1 GFLOP (20 us of element-wise work) the copies (two
 // short launches and one pass over A and B) pay for themselves many times.
+// The transposing copy moves 64 x 64 blocks through LDS; it is priced at this
+// fraction of the HBM rate.
+static constexpr double kTransposeHbmFrac = 0.6;
+
 static bool pack_worthwhile(const Problem &p)
 {
     return p.M > 1 && p.N > 1 && 2.0 * (double)p.M * (double)p.N * (double)p.K >= 1e9;
@@ -603,15 +636,45 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
         out->pred_us = 0.0;
         return TG_OK;
     }
+    // float32 copies are laid out for the NT product, whose 256 x 256 kernel
+    // is the fastest float32 one
+    const bool nt = p.dtype == TG_F32 && p.trans != TG_NT;
+    const bool forced_other = opts && opts->path != TG_PATH_AUTO && opts->path != TG_PATH_MFMA;
+    if (allow_pack && nt && vec_ok(p) && pack_worthwhile(p) && !forced_other) {
+        // aligned float32 in another layout: the direct plan, or a transposed
+        // copy of the operand(s) stored M/N-contiguous and the NT plan,
+        // whichever the model prices lower
+        tg_plan direct;
+        const int rc_d = make_plan(p, chip, occupancy, opts, occ, occ_ctx, model, &direct, why, false);
+        const Problem q = packed_problem(p, true);
+        const PackLayout L = pack_layout(p, true);
+        tg_plan inner;
+        const char *why_n = none;
+        const int rc_n = make_plan(q, chip, occupancy, opts, occ, occ_ctx, model, &inner, &why_n, false);
+        const double copy_us = 2.0 * (double)L.bytes / (chip.hbm_gbs * 1e3 * kTransposeHbmFrac) +
+                               (L.a_copy + L.b_copy) * chip.launch_us;
+        if (rc_n == TG_OK && inner.vector_io == 1 &&
+            (rc_d != TG_OK || inner.pred_us + copy_us < direct.pred_us)) {
+            *out = inner;
+            out->vector_io = 3;
+            out->workspace_bytes = L.bytes + inner.workspace_bytes;
+            out->pred_us += copy_us;
+            fill_common(p, chip, out);
+            *why = none;
+            return TG_OK;
+        }
+        if (rc_d == TG_OK)
+            *out = direct;
+        return rc_d;
+    }
     if (allow_pack && !vec_ok(p) && pack_worthwhile(p) && !(opts && opts->path == TG_PATH_GEMV)) {
         // plan the padded, aligned copy ("Matrix Multiplication Background
         // User's Guide", section 3.1: multiples of 8 elements keep the matrix
         // units fed; padding is how a caller gets there)
-        const Problem q = packed_problem(p);
-        const PackLayout L = pack_layout(p);
+        const Problem q = packed_problem(p, nt);
+        const PackLayout L = pack_layout(p, nt);
         tg_plan inner;
         int rc = make_plan(q, chip, occupancy, opts, occ, occ_ctx, model, &inner, why, false);
-        const bool forced_other = opts && opts->path != TG_PATH_AUTO && opts->path != TG_PATH_MFMA;
         if (L.padded_mn && forced_other)
             rc = TG_ERR_UNSUPPORTED;  // the forced path keeps its own element-wise form
         else if (rc == TG_OK && L.padded_mn && inner.path != TG_PATH_MFMA) {
@@ -622,7 +685,7 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
         }
         if (rc == TG_OK && inner.vector_io == 1) {
             *out = inner;
-            out->vector_io = 2;
+            out->vector_io = nt ? 3 : 2;
             out->workspace_bytes = L.bytes + inner.workspace_bytes;
             out->pred_us += 2.0 * (double)L.bytes / (chip.hbm_gbs * 1e3) + 2.0 * chip.launch_us;
             fill_common(p, chip, out);

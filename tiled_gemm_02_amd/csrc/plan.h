@@ -76,15 +76,23 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
 // macro-tile kernel runs the product: it reads the copies over their padded
 // extent and stores the M x N result straight into C (its stores are bounded
 // by M and N, its loads by M' and N').
+//
+// nt (float32 in a layout other than NT, plan vector_io == 3): the copies are
+// laid out K-contiguous, A' = M' x K' and B' = N' x K', transposing the
+// operands stored the other way, and the product runs as NT.  An aligned
+// problem copies only the operands that need the transpose (no padding); the
+// other is read in place.
 struct PackLayout {
-    int64_t a_rows, a_cols;   // stored A' (row-major): (trans_a ? K' x M' : M' x K')
-    int64_t b_rows, b_cols;   // stored B': (trans_b ? N' x K' : K' x N')
+    int64_t a_rows, a_cols;   // stored A' (row-major): (trans_a ? K' x M' : M' x K'); nt: M' x K'
+    int64_t b_rows, b_cols;   // stored B': (trans_b ? N' x K' : K' x N'); nt: N' x K'
     uint64_t a_off, b_off;    // byte offsets in the workspace
-    uint64_t bytes;           // both buffers; the kernels' own workspace follows
+    uint64_t bytes;           // the copies; the kernels' own workspace follows
     bool padded_mn;           // M or N rounded up
+    bool a_copy, b_copy;      // operand copied (else read in place)
+    bool a_trans, b_trans;    // copy transposes the stored operand
 };
-PackLayout pack_layout(const Problem &p);
-Problem packed_problem(const Problem &p);
+PackLayout pack_layout(const Problem &p, bool nt = false);
+Problem packed_problem(const Problem &p, bool nt = false);
 
 // 16-byte-chunk element count of a storage type.
 inline int chunk_elems(int dtype) { return dtype == TG_F32 ? 4 : 8; }
