@@ -606,7 +606,9 @@ def test_unaligned_operands_copied(case):
     M, N, K, dtype, trans, pad = case
     _say("case aligned copy", case)
     p = make_problem(M, N, K, dtype, trans, "uniform", seed=51, ld_pad=pad)
-    assert tg.tg_plan_model(M, N, K, dtype, trans)["vector_io"] == 2
+    # float32 in a layout other than NT copies into the NT layout (3)
+    want = 3 if dtype == F32 and trans != NT else 2
+    assert tg.tg_plan_model(M, N, K, dtype, trans)["vector_io"] == want
     r, _, _ = check_full(p)
     assert r["ok"], (case, r)
     r, _, _ = check_scaled(p, 0.5, -1.0, epilogue="leaky_relu", c_seed=6)
@@ -634,7 +636,8 @@ def test_unaligned_rows_and_columns_copied(case):
     _say("case padded copy", case)
     p = make_problem(M, N, K, dtype, trans, "uniform", seed=53, ld_pad=pad)
     pl = tg.tg_plan_model(M, N, K, dtype, trans)
-    assert pl["vector_io"] == 2 and pl["path_name"] == "mfma"
+    want = 3 if dtype == F32 and trans != NT else 2
+    assert pl["vector_io"] == want and pl["path_name"] == "mfma"
     r, _, _ = check_full(p, out_pad=3)
     assert r["ok"], (case, r)
     r, _, _ = check_scaled(p, 0.5, -1.0, epilogue="leaky_relu", c_seed=7)
