@@ -140,7 +140,7 @@ def test_leaky_relu_epilogue(dtype, trans):
 def _tiles(dtype, trans):
     if dtype == F32:   # the float32 256 x 256 kernel takes K-contiguous A and B only
         return ([(256, 256)] if trans == NT else []) + [(128, 128), (64, 64)]
-    return [(256, 256), (256, 128), (128, 128), (128, 64), (64, 64)]
+    return [(256, 256), (192, 256), (256, 128), (128, 128), (128, 64), (64, 64)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -162,6 +162,45 @@ def test_every_tile(dtype, trans):
         p = make_problem(296, 280, 136, dtype, trans, "normal", seed=6)
         with pytest.raises(tg.TgError):
             run_gpu(p, options=dict(tile_m=256, tile_n=256))
+
+
+# 16-bit 192 x 256 tiles (the ping-pong kernel with 96 x 64 per wave, A
+# K-contiguous): ragged edges, K tails, splits, alpha / beta with the
+# epilogue; stored-transposed A is refused
+TILE192_CASES = [
+    (400, 520, 1000, F16, NN, 1, None, 1.0, 0.0),
+    (200, 304, 72, BF16, NT, 1, None, 1.0, 0.0),
+    (584, 264, 1032, F16, NT, 3, None, 1.0, 0.0),
+    (384, 512, 512, BF16, NN, 2, "leaky_relu", 0.5, -1.0),
+]
+
+
+@pytest.mark.parametrize("case", TILE192_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}-s{c[5]}")
+def test_tile_192x256(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, dtype, trans, split, epi, alpha, beta = case
+    _say("case tile 192", case)
+    p = make_problem(M, N, K, dtype, trans, "normal", seed=31)
+    opts = dict(tile_m=192, tile_n=256, split_k=split)
+    if alpha == 1.0 and beta == 0.0:
+        r, _, _ = check_full(p, epilogue=epi, options=opts)
+    else:
+        r, _, _ = check_scaled(p, alpha, beta, epilogue=epi, options=opts)
+    assert r["ok"], (case, r)
+    q = make_problem(M, N, K, dtype, TN, "normal", seed=31)
+    with pytest.raises(tg.TgError):
+        run_gpu(q, options=opts)
+
+
+def test_tile_192x256_is_planned_and_sampled():
+    """2304 x 4096 x 4096: 192 tiles of 192 x 256 against 144 of 256 x 256."""
+    import tiled_gemm_02_amd as tg
+    pl = tg.tg_gemm_plan(2304, 4096, 4096, tg.TG_F16, tg.TG_NN)
+    assert (pl["tile_m"], pl["tile_n"], pl["tiles"]) == (192, 256, 192), pl
+    p = make_problem(2304, 4096, 4096, F16, NN, "normal", seed=0)
+    _say("case tile 192 sampled")
+    r = check_sampled(p, n=2048)
+    assert r["ok"], r
 
 
 # float32 on the 256 x 256 ping-pong kernel: ragged M and N edges, a K tail

@@ -84,6 +84,8 @@ static bool use_mfma2(int dtype, int trans, bool vec, int bm, int bn, int64_t ld
         return false;
     if (dtype == TG_F32)
         return bm == 256 && bn == 256 && trans == TG_NT;
+    if (bm == 192)
+        return true;   // the 192 x 256 tile exists on the ping-pong kernel only
     return mfma_variant() == 2;
 }
 

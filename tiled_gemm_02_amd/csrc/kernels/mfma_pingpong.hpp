@@ -21,6 +21,10 @@
 // unit always has one wave with nothing to wait for, and the LDS reads, the
 // copy issue and their latencies hide behind the other wave's MFMAs.
 //
+// 192 x 256 tiles (K-contiguous 16-bit A): each wave owns 96 x 64 (6 x 4
+// blocks), group 0 copies three 1 KiB pieces of A per stage and group 1 four
+// of B, so each group waits for its own count.
+//
 // Copies.  Group 0 copies A, group 1 copies B.  In its load phase of stage b a
 // group refills the buffer of stage b - 2 with stage b + S - 2.  Stage b - 2
 // was last read in phase 2b - 3, and those reads completed before the MFMAs
@@ -83,14 +87,18 @@ __device__ __forceinline__ uint32_t mn32_base(uint32_t st, int ks, int h, int la
     return st + (uint32_t)((k * CH + c) * 16 + (n & 7) * 2);
 }
 
-template <typename Tr, int S, int MI, bool TA, bool TB, bool SK = false>
+template <typename Tr, int S, int MI, bool TA, bool TB, bool SK = false, int BM = 256>
 __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = typename Tr::T;
-    constexpr int BM = 256, BN = 256, BKS = 32;
+    constexpr int BN = 256, BKS = 32;
     constexpr int WGN = 4;
-    constexpr int WM = 128, WN = 64;
+    constexpr int WM = BM / 2, WN = 64;
+    // 192 x 256 tiles (96 x 64 per wave): A K-contiguous (its M/N-contiguous
+    // LDS layout needs a power-of-two row of chunks), 16-bit, no stream-K
+    static_assert(BM == 256 || (BM == 192 && !TA && !SK && MI == 16 && Tr::kBytes == 2),
+                  "192-row tiles: K-contiguous 16-bit A only");
     static_assert(MI == 16 || MI == 32, "MFMA block edge");
     constexpr int FM = WM / MI, FN = WN / MI;            // blocks per wave (8 x 4 or 4 x 2)
     constexpr int KS = BKS * MI / 512;                   // K steps per stage (1 or 2)
@@ -99,9 +107,9 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
     using OpB = Dma3<BN, !TB, 4, BKS, SW>;               // copied by group 1
     constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
     constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int NDMA = OpA::PER_WAVE;                  // copies per wave per stage
-    static_assert(OpA::PER_WAVE == OpB::PER_WAVE, "both groups copy the same amount");
-    static_assert(S >= 3 && S <= 5 && (S - 2) * NDMA < 64, "stage count");
+    // copies per wave per stage: group 0 (A) and group 1 (B); equal for 256 x 256
+    constexpr int NDMA_A = OpA::PER_WAVE, NDMA_B = OpB::PER_WAVE;
+    static_assert(S >= 3 && S <= 5 && (S - 2) * (NDMA_A > NDMA_B ? NDMA_A : NDMA_B) < 64, "stage count");
     // float32 operands are copied as pairs of 16-bit units: a stage row is
     // then 16 values of K, and only K-contiguous operands are supported (the
     // transposed LDS reads of the M/N-contiguous layouts are 16-bit reads)
@@ -157,7 +165,8 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
         // `last` having been issued: the younger stages (all DMA) may stay in
         // flight.  `lds` also waits for this wave's LDS traffic (the prologue's
         // register-path writes).
-        auto wait_stage = [&](int t, int last, bool lds_too) {
+        auto wait_stage_n = [&](auto ndma, int t, int last, bool lds_too) {
+            constexpr int NDMA = decltype(ndma)::value;
             const int younger = max(0, min(last - t, S - 2));
             if (lds_too) {
                 if (S >= 5 && younger >= 3)
@@ -178,6 +187,14 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
                 else
                     wait_vm<0>();
             }
+        };
+        auto wait_stage = [&](int t, int last, bool lds_too) {
+            if constexpr (NDMA_A == NDMA_B)
+                wait_stage_n(std::integral_constant<int, NDMA_A>{}, t, last, lds_too);
+            else if (grp == 0)
+                wait_stage_n(std::integral_constant<int, NDMA_A>{}, t, last, lds_too);
+            else
+                wait_stage_n(std::integral_constant<int, NDMA_B>{}, t, last, lds_too);
         };
 
         // fragment reads of one stage: (K step, row block) for A, (K step,

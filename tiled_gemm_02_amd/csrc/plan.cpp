@@ -30,7 +30,7 @@ namespace tg {
 // ping-pong kernel, about 1250 TFLOP/s under the board's power limit; the
 // others: the 4-wave LDS-DMA kernel).
 static const TileSpec kTiles16[] = {
-    {256, 256, 0.50, 160}, {256, 128, 0.355, 96}, {128, 128, 0.385, 64},
+    {256, 256, 0.50, 160}, {192, 256, 0.42, 140}, {256, 128, 0.355, 96}, {128, 128, 0.385, 64},
     {128, 64, 0.31, 48},   {64, 64, 0.22, 32},
 };
 // float32: 256 x 256 is the ping-pong kernel, K-contiguous A and B only
@@ -70,6 +70,9 @@ static bool tile_fits(const Problem &p, int bm, int bn)
 {
     if (p.dtype == TG_F32 && bm == 256 && bn == 256)
         return p.trans == TG_NT && p.lda <= (1 << 21) && p.ldb <= (1 << 21);
+    // 192 x 256: the ping-pong kernel with K-contiguous A
+    if (bm == 192 && bn == 256)
+        return p.dtype != TG_F32 && !(p.trans & TG_TRANS_A) && p.lda <= (1 << 22) && p.ldb <= (1 << 22);
     return true;
 }
 
