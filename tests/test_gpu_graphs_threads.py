@@ -12,7 +12,7 @@ import threading
 import numpy as np
 import pytest
 
-from gemm_inputs import F16, NN, NT, make_problem, make_softmax_input
+from gemm_inputs import F16, F32, NN, NT, make_problem, make_softmax_input
 from tests.gpu_helpers import to_device
 
 pytestmark = pytest.mark.gpu
@@ -28,16 +28,21 @@ def test_graph_capture_replays_match_eager():
     _say("case graph capture")
     dev = torch.device("cuda:0")
     # a whole-tile product, a split-K product (reduction kernel), a stream-K
-    # product (fix-up kernel) and a row softmax, all with caller workspace
+    # product (fix-up kernel), 192 x 256 tiles, a float32 NN product through
+    # its transposing copy, and a row softmax, all with caller workspace
     probs = [(make_problem(1024, 1024, 1024, F16, NN, "normal", seed=71), None),
              (make_problem(256, 256, 8192, F16, NT, "normal", seed=72), dict(split_k=8)),
              (make_problem(1024, 1024, 4096, F16, NN, "normal", seed=73),
-              dict(split_k=tg.TG_SPLIT_STREAM_K))]
+              dict(split_k=tg.TG_SPLIT_STREAM_K)),
+             (make_problem(768, 1024, 1024, F16, NN, "normal", seed=75), dict(tile_m=192, tile_n=256)),
+             (make_problem(1024, 1024, 1024, F32, NN, "normal", seed=76), dict(tile_m=256, tile_n=256))]
+    assert tg.tg_gemm_plan(1024, 1024, 1024, tg.TG_F32, tg.TG_NN,
+                           options=dict(tile_m=256, tile_n=256))["vector_io"] == 3
     ins = [(to_device(p.A, p.dtype), to_device(p.B, p.dtype), o, p) for p, o in probs]
     sp = make_softmax_input(300, 4000, F16, "normal", seed=74)
     X = to_device(sp.X, sp.dtype)
     ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-    outs = [torch.empty((p.M, p.N), dtype=torch.float16, device=dev) for _, _, _, p in ins]
+    outs = [torch.empty((p.M, p.N), dtype=A.dtype, device=dev) for A, _, _, p in ins]
     Y = torch.empty_like(X)
 
     def work(stream):
@@ -60,7 +65,8 @@ def test_graph_capture_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         for i, (e, t) in enumerate(zip(eager, outs + [Y])):
-            assert torch.equal(e.view(torch.int16), t.view(torch.int16)), (rep, i)
+            bits = torch.int32 if e.dtype == torch.float32 else torch.int16
+            assert torch.equal(e.view(bits), t.view(bits)), (rep, i)
 
 
 def test_calls_from_several_threads():
@@ -70,10 +76,13 @@ def test_calls_from_several_threads():
     dev = torch.device("cuda:0")
     probs = [make_problem(512 + 64 * i, 768, 1024 + 256 * i, F16, NN, "normal", seed=80 + i)
              for i in range(4)]
+    # and a float32 NN product through its transposing copy (workspace per call)
+    probs.append(make_problem(1024, 1024, 1024, F32, NN, "normal", seed=85))
+    opts = [None] * 4 + [dict(tile_m=256, tile_n=256)]
     devs = [(to_device(p.A, p.dtype), to_device(p.B, p.dtype)) for p in probs]
     ref = []
-    for (A, B) in devs:
-        ref.append(tg.gemm(A, B))
+    for (A, B), o in zip(devs, opts):
+        ref.append(tg.gemm(A, B, options=o))
     torch.cuda.synchronize()
     outs = [torch.empty_like(r) for r in ref]
     errors = []
@@ -83,16 +92,17 @@ def test_calls_from_several_threads():
             s = torch.cuda.Stream(device=dev)
             A, B = devs[i]
             for _ in range(20):
-                tg.gemm(A, B, out=outs[i], stream=s.cuda_stream)
+                tg.gemm(A, B, out=outs[i], options=opts[i], stream=s.cuda_stream)
             s.synchronize()
         except Exception as e:   # reported below
             errors.append((i, repr(e)))
 
-    th = [threading.Thread(target=run, args=(i,)) for i in range(4)]
+    th = [threading.Thread(target=run, args=(i,)) for i in range(len(probs))]
     for t in th:
         t.start()
     for t in th:
         t.join()
     assert not errors, errors
     for r, o in zip(ref, outs):
-        assert torch.equal(r.view(torch.int16), o.view(torch.int16))
+        bits = torch.int32 if r.dtype == torch.float32 else torch.int16
+        assert torch.equal(r.view(bits), o.view(bits))
