@@ -307,7 +307,7 @@ static int tile_slot(int bm, int bn)
 {
     // index of the tile in a small fixed table used for the occupancy cache
     static const int tiles[8][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64},
-                                    {64, 64},   {128, 256}, {64, 128},  {32, 32}};
+                                    {64, 64},   {128, 256}, {64, 128},  {192, 256}};
     for (int i = 0; i < 8; ++i)
         if (tiles[i][0] == bm && tiles[i][1] == bn)
             return i;

@@ -53,18 +53,6 @@ int tile_menu(int dtype, const TileSpec **out)
     return (int)(sizeof kTiles16 / sizeof kTiles16[0]);
 }
 
-bool has_mfma_tile(int dtype, int bm, int bn, bool vec)
-{
-    if (!vec)
-        return bm == 64 && bn == 64;
-    const TileSpec *t;
-    int n = tile_menu(dtype, &t);
-    for (int i = 0; i < n; ++i)
-        if (t[i].bm == bm && t[i].bn == bn)
-            return true;
-    return false;
-}
-
 // Whether the kernel behind a menu tile takes this problem's layout.
 static bool tile_fits(const Problem &p, int bm, int bn)
 {

@@ -41,7 +41,6 @@ struct TileSpec {
 };
 
 int tile_menu(int dtype, const TileSpec **out);       // vector-load tiles, largest first
-bool has_mfma_tile(int dtype, int bm, int bn, bool vec);
 
 // Residency of a tile kernel on one CU when no measured value is given:
 // limited by LDS (160 KiB per CU) and the kernels' register use.
