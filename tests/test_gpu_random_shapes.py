@@ -1,0 +1,78 @@
+"""Seeded random products against the float64 oracle (run with -m gpu).
+
+A fixed list of cases drawn from one seed: sizes from 1 to 700 in every
+dimension (aligned and not, so the vector, padded-copy and element-wise loads
+all occur), every storage type and layout, padded leading dimensions, the
+LeakyReLU epilogue, alpha / beta, and forced K splits or tiles where the
+operands allow them.  Every output element is compared with the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from gemm_inputs import BF16, F16, F32, NN, NT, TN, TT, make_problem
+from tests.gpu_helpers import check_full, check_scaled
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n=200, seed=2024):
+    rng = np.random.default_rng(seed)
+
+    def pick(xs):
+        return xs[int(rng.integers(0, len(xs)))]
+
+    def dim(lo=1, hi=700):
+        # half the draws on the 16-byte grid of every type, half anywhere
+        if rng.random() < 0.5:
+            return int(rng.integers(max(1, lo // 8), hi // 8 + 1)) * 8
+        return int(rng.integers(lo, hi + 1))
+
+    out = []
+    for i in range(n):
+        kind = rng.random()
+        dtype = pick([F32, F16, BF16])
+        trans = pick([NN, NT, TN, TT])
+        pad = pick([0, 0, 3, 6])
+        opt = None
+        if kind < 0.4:                       # anything
+            M, N, K = dim(), dim(), dim()
+            if rng.random() < 0.25 and K >= 64:
+                opt = dict(split_k=int(rng.integers(2, 5)))
+        elif kind < 0.55:                    # narrow outputs (skinny path when 16-bit)
+            dtype, trans, pad = pick([F16, BF16]), pick([NN, NT]), 0
+            M, N, K = int(rng.integers(32, 257)) * 8, int(rng.integers(1, 17)) * 8, int(rng.integers(8, 129)) * 8
+        elif kind < 0.7:                     # GEMV forms
+            M, N, K = (1, dim(1, 2000), dim(1, 1500)) if rng.random() < 0.5 else (dim(1, 2000), 1, dim(1, 1500))
+        elif kind < 0.8:                     # large enough for the aligned copies
+            M, N, K = dim(1000, 1100), dim(1000, 1100), dim(1000, 1100)
+        else:                                # aligned operands, forced tiles
+            pad = 0
+            M, N, K = int(rng.integers(1, 80)) * 8, int(rng.integers(1, 80)) * 8, int(rng.integers(1, 80)) * 8
+            if dtype == F32:
+                tiles = [(128, 128), (64, 64)] + ([(256, 256)] if trans == NT else [])
+            else:
+                tiles = [(256, 256), (256, 128), (128, 128), (128, 64), (64, 64)] + \
+                        ([(192, 256)] if not (trans & 1) else [])
+            tm, tn = pick(tiles)
+            opt = dict(tile_m=tm, tile_n=tn, split_k=int(rng.integers(1, 4)))
+        epi = "leaky_relu" if rng.random() < 0.3 else None
+        scaled = rng.random() < 0.3
+        out.append((i, M, N, K, dtype, trans, pad, epi, scaled, opt))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-d{c[4]}-t{c[5]}")
+def test_random_product(case):
+    i, M, N, K, dtype, trans, pad, epi, scaled, opt = case
+    print("case random", case, flush=True)
+    p = make_problem(M, N, K, dtype, trans, "normal", seed=1000 + i, ld_pad=pad)
+    if scaled:
+        r, _, _ = check_scaled(p, 0.75, -1.25, epilogue=epi, options=opt, c_seed=i)
+    else:
+        r, _, _ = check_full(p, epilogue=epi, options=opt)
+    assert r["ok"], (case, r)
