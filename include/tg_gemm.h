@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 104
+#define TG_VERSION 105
 
 /* storage type of A, B and C */
 enum tg_dtype { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 };
@@ -158,9 +158,10 @@ typedef struct tg_plan {
 
 /* C = epi(alpha A . B + beta C) on the current HIP device.  epilogue may be
  * NULL (C = A . B).  When the plan needs workspace (float32 split-K partials,
- * or aligned copies of A and B), it is a stream-ordered allocation on
- * `stream` from a memory pool the library keeps per device: memory a call
- * frees stays reserved for later calls until the process ends. */
+ * or aligned copies of A and B), it comes from the calling thread's default
+ * workspace (tg_set_workspace) when one is set, else it is a stream-ordered
+ * allocation on `stream` from a memory pool the library keeps per device:
+ * memory a call frees stays reserved for later calls until the process ends. */
 int tg_gemm(int64_t M, int64_t N, int64_t K,
             const void *A, int64_t lda,
             const void *B, int64_t ldb,
@@ -170,7 +171,7 @@ int tg_gemm(int64_t M, int64_t N, int64_t K,
             void *stream);
 
 /* tg_gemm with planner overrides and a caller-provided workspace.
- * workspace == NULL: as tg_gemm.  Otherwise it must be device memory aligned
+ * workspace == NULL: as tg_gemm (the thread's default workspace, if set).  Otherwise it must be device memory aligned
  * to 256 bytes; when smaller than the plan's workspace_bytes the planner
  * falls back to an unsplit plan (not an error unless split_k was forced, then
  * TG_ERR_ARG).  Concurrent calls must not share a workspace. */
@@ -198,6 +199,22 @@ int tg_plan_model(int64_t M, int64_t N, int64_t K, int dtype, int trans,
 /* Bytes of workspace the current device's plan needs (0 = none). */
 size_t tg_workspace_size(int64_t M, int64_t N, int64_t K, int dtype, int trans,
                          const tg_options *opts);
+
+/* The same for the planner's own choice (no overrides): the size of the
+ * buffer of K-split partials ("Matrix Multiplication Background User's
+ * Guide", section 2.3: a split adds a reduction over float32 partial tiles)
+ * and of any aligned operand copies. */
+size_t tg_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype, int trans);
+
+/* Set the calling thread's default workspace: device memory of `bytes`
+ * bytes, aligned to 256 bytes, owned by the caller and used (not copied) by
+ * every later tg_gemm, and by tg_gemm_ex / tg_autotune calls whose own
+ * workspace is NULL, until replaced; (NULL, 0) clears it.  A plan that needs
+ * more than `bytes` falls back as with a small tg_gemm_ex workspace.  The
+ * buffer holds partials only for the duration of each call on its stream:
+ * calls that may overlap (other streams) need workspaces of their own.
+ * Returns TG_ERR_ARG for a misaligned buffer, or NULL with bytes > 0. */
+int tg_set_workspace(void *workspace, size_t bytes);
 
 /* Benchmark mode ("Matrix Multiplication Background User's Guide", section
  * 2.3: a library may time its candidate kernels instead of trusting its

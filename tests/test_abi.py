@@ -22,7 +22,8 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for must in ("tg_gemm", "tg_gemm_ex", "tg_gemm_plan", "tg_plan_model", "tg_workspace_size",
-                 "tg_device_cus", "tg_last_error", "tg_version"):
+                 "tg_workspace_bytes", "tg_set_workspace", "tg_device_cus", "tg_last_error",
+                 "tg_version"):
         assert must in names
 
 
@@ -33,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert tg.tg_version() == 104
+    assert tg.tg_version() == 105
 
 
 def test_epilogue_struct_matches_header(tmp_path):
@@ -106,3 +107,13 @@ def test_plan_model_rejects_bad_input():
         tg.tg_plan_model(4, 4, 4, tg.TG_F16, options=dict(path=tg.TG_PATH_GEMV))
     with pytest.raises(tg.TgError):
         tg.tg_plan_model(4, 4, 4, tg.TG_F16, options=dict(tile_m=64))
+
+
+def test_set_workspace_argument_checks():
+    """tg_set_workspace needs no device: NULL with a size and a misaligned
+    pointer are argument errors; (NULL, 0) clears."""
+    with pytest.raises(tg.TgError):
+        tg.tg_set_workspace(None, 1024)
+    with pytest.raises(tg.TgError):
+        tg.tg_set_workspace(0x1000 + 16, 1024)
+    assert tg.tg_set_workspace(None, 0) == 0

@@ -297,6 +297,34 @@ def test_split_k_caller_workspace():
     assert r["ok"], r
 
 
+def test_thread_default_workspace():
+    """tg_set_workspace: calls without a workspace of their own use the
+    thread's default; one too small for a forced split is an error, an
+    unforced plan falls back; cleared, the library allocates again."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    _say("case default workspace")
+    p = make_problem(256, 256, 8192, F16, NT, "normal", seed=91)
+    need = tg.tg_workspace_size(256, 256, 8192, tg.TG_F16, tg.TG_NT, dict(split_k=8))
+    assert need == 8 * 256 * 256 * 4
+    assert tg.tg_workspace_bytes(256, 256, 8192, tg.TG_F16, tg.TG_NT) == \
+        tg.tg_workspace_size(256, 256, 8192, tg.TG_F16, tg.TG_NT)
+    buf = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    try:
+        tg.set_workspace(buf)
+        r, _, _ = check_full(p, options=dict(split_k=8))
+        assert r["ok"], r
+        tg.set_workspace(buf[:1024])
+        with pytest.raises(tg.TgError):
+            run_gpu(p, options=dict(split_k=8))
+        r, _, _ = check_full(p)
+        assert r["ok"], r
+    finally:
+        tg.set_workspace(None)
+    r, _, _ = check_full(p, options=dict(split_k=8))
+    assert r["ok"], r
+
+
 @pytest.mark.parametrize("case", ["gemv", "skinny"])
 def test_split_partials_ignore_stale_workspace(case):
     """K-split partials are fully rewritten by every call: arbitrary bytes left

@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtg_gemm.so")
@@ -89,6 +90,10 @@ def load():
     lib.tg_plan_model.restype = i32
     lib.tg_workspace_size.argtypes = [i64, i64, i64, i32, i32, op]
     lib.tg_workspace_size.restype = ctypes.c_size_t
+    lib.tg_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    lib.tg_workspace_bytes.restype = ctypes.c_size_t
+    lib.tg_set_workspace.argtypes = [vp, ctypes.c_size_t]
+    lib.tg_set_workspace.restype = i32
     lib.tg_softmax.argtypes = [i64, i64, vp, i64, vp, i64, i32, vp]
     lib.tg_softmax.restype = i32
     lib.tg_softmax_shape.argtypes = [i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -184,6 +189,14 @@ def tg_workspace_size(M, N, K, dtype, trans=TG_NN, options=None) -> int:
     return int(load().tg_workspace_size(M, N, K, dtype, trans, _opts(options)))
 
 
+def tg_workspace_bytes(M, N, K, dtype, trans=TG_NN) -> int:
+    return int(load().tg_workspace_bytes(M, N, K, dtype, trans))
+
+
+def tg_set_workspace(ptr, nbytes: int) -> int:
+    return _check(load().tg_set_workspace(ptr, nbytes))
+
+
 def tg_device_cus() -> int:
     return int(load().tg_device_cus())
 
@@ -275,6 +288,21 @@ def softmax(X, *, out=None, stream=None):
         stream = torch.cuda.current_stream(X.device).cuda_stream
     _check(load().tg_softmax(M, N, X.data_ptr(), _ld(X), out.data_ptr(), _ld(out), dtype, stream))
     return out
+
+
+_ws_keep = threading.local()
+
+
+def set_workspace(buf) -> None:
+    """Make the uint8 device tensor ``buf`` the calling thread's default
+    workspace (tg_set_workspace); None clears it.  The tensor is kept alive
+    until replaced."""
+    if buf is None:
+        tg_set_workspace(None, 0)
+        _ws_keep.buf = None
+        return
+    tg_set_workspace(buf.data_ptr(), buf.numel() * buf.element_size())
+    _ws_keep.buf = buf
 
 
 def tune_cache_clear() -> None:

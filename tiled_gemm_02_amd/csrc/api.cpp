@@ -541,11 +541,19 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
     return TG_OK;
 }
 
+// The calling thread's default workspace (tg_set_workspace).
+static thread_local void *t_ws = nullptr;
+static thread_local size_t t_ws_bytes = 0;
+
 static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                      int64_t ldb, void *C, int64_t ldc, int dtype, int trans,
                      const tg_epilogue *epi, const tg_options *opts, void *user_ws,
                      size_t user_ws_bytes, void *stream)
 {
+    if (!user_ws) {
+        user_ws = t_ws;
+        user_ws_bytes = t_ws_bytes;
+    }
     int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epi);
     if (rc != TG_OK)
         return rc;
@@ -733,6 +741,22 @@ size_t tg_workspace_size(int64_t M, int64_t N, int64_t K, int dtype, int trans,
     if (tg_gemm_plan(M, N, K, dtype, trans, opts, &pl) != TG_OK)
         return 0;
     return (size_t)pl.workspace_bytes;
+}
+
+size_t tg_workspace_bytes(int64_t M, int64_t N, int64_t K, int dtype, int trans)
+{
+    return tg_workspace_size(M, N, K, dtype, trans, nullptr);
+}
+
+int tg_set_workspace(void *workspace, size_t bytes)
+{
+    if (!workspace && bytes > 0)
+        return fail(TG_ERR_ARG, "workspace is NULL but bytes = %zu", bytes);
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(TG_ERR_ARG, "workspace must be 256-byte aligned");
+    t_ws = workspace;
+    t_ws_bytes = workspace ? bytes : 0;
+    return ok();
 }
 
 int tg_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
