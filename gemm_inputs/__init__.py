@@ -220,6 +220,10 @@ WORKLOADS = {
                             epilogue="leaky_relu", slope=0.01),
     "bf16_leaky_6912x2048x4096": dict(M=6912, N=2048, K=4096, dtype=BF16, trans=NN, dist="normal",
                                       seed=1, epilogue="leaky_relu", slope=0.01),
+    # float32 at the headline size: NT (the 256 x 256 kernel directly) and NN
+    # (through the transposing copy of B)
+    "f32_8192_nt": dict(M=8192, N=8192, K=8192, dtype=F32, trans=NT, dist="normal", seed=1),
+    "f32_8192": dict(M=8192, N=8192, K=8192, dtype=F32, trans=NN, dist="normal", seed=1),
     # the full BLAS statement C = alpha A.B + beta C_old (C_old from make_c_old, seed 1)
     "f16_8192_alpha_beta": dict(M=8192, N=8192, K=8192, dtype=F16, trans=NN, dist="normal", seed=1,
                                 alpha=0.5, beta=1.0),
