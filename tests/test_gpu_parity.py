@@ -460,7 +460,7 @@ def test_workload_full(name):
 
 
 @pytest.mark.parametrize("name", ["f16_4096_nt", "f16_8192", "bf16_leaky_8192",
-                                  "bf16_leaky_6912x2048x4096"])
+                                  "bf16_leaky_6912x2048x4096", "f32_8192_nt", "f32_8192"])
 def test_workload_sampled(name):
     w = dict(WORKLOADS[name])
     _say("workload sampled", name)
