@@ -624,8 +624,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="f16_8192")
     ap.add_argument("--secondary", default="f16_skinny_8192x128x8192,f16_gemv_1x8192x8192,"
-                    "softmax_f32_4096x32768,softmax_f16_4096x32768",
-                    help="comma-separated memory-bound workloads reported alongside ('' for none)")
+                    "softmax_f32_4096x32768,softmax_f16_4096x32768,f16_4096_nt,f32_8192_nt",
+                    help="comma-separated workloads reported alongside ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", default=None,
@@ -726,9 +726,11 @@ def main():
             del rs
             torch.cuda.empty_cache()
             continue
-        rs = time_workload(name, max(args.steps, 50), args.warmup, device, rotate=True)
-        ent = roofline_entry(rs, "hbm")
-        sec.append({"workload": name, "value": ent["achieved"], "unit": "GB/s",
+        ws = WORKLOADS[name]
+        sec_mem = ws["N"] <= 256 or ws["M"] == 1
+        rs = time_workload(name, max(args.steps, 50), args.warmup, device, rotate=sec_mem)
+        ent = roofline_entry(rs, "hbm" if sec_mem else "mfma")
+        sec.append({"workload": name, "value": ent["achieved"], "unit": ent["unit"],
                     "ms_per_step": round(rs["ms_per_step"], 5),
                     "plan": {k: rs["plan"][k] for k in ("path_name", "tile_m", "tile_n", "split_k",
                                                          "workgroups")},
