@@ -258,7 +258,7 @@ def roofline_entry(r, bound):
 # changed kernel reports null until it is measured again.
 
 TRAFFIC_WORKLOADS = ["f16_8192", "f16_skinny_8192x128x8192", "f16_gemv_1x8192x8192",
-                     "softmax_f32_4096x32768", "softmax_f16_4096x32768"]
+                     "softmax_f32_4096x32768", "softmax_f16_4096x32768", "f16_4096_nt", "f32_8192_nt"]
 COPY_BYTES = 256 << 20
 DOMINANT = {"mfma": "mfma_", "skinny": "skinny_kernel", "softmax": "softmax_rows_kernel"}
 # GEMV: gemv_cols / gemv_rows
