@@ -199,7 +199,7 @@ def test_tile_192x256_is_planned_and_sampled():
     assert (pl["tile_m"], pl["tile_n"], pl["tiles"]) == (192, 256, 192), pl
     p = make_problem(2304, 4096, 4096, F16, NN, "normal", seed=0)
     _say("case tile 192 sampled")
-    r = check_sampled(p, n=2048)
+    r = check_sampled(p)
     assert r["ok"], r
 
 
@@ -267,7 +267,7 @@ def test_f32_pingpong_is_planned_and_sampled():
         pl = tg.tg_gemm_plan(p.M, p.N, p.K, tg.TG_F32, trans)
         assert (pl["tile_m"], pl["tile_n"], pl["vector_io"]) == (256, 256, vio), pl
         _say("case f32 4096 sampled", trans)
-        r = check_sampled(p, n=2048)
+        r = check_sampled(p)
         assert r["ok"], r
 
 
@@ -475,9 +475,9 @@ def test_workload_sampled(name):
 def test_sweep_shapes_sampled(N):
     _say("sweep", N)
     p = make_problem(2304, N, 4096, F16, NN, "normal", seed=0)
-    r = check_sampled(p, n=2048)
+    r = check_sampled(p)
     assert r["ok"], r
-    r = check_sampled(p, n=1024, options=dict(tile_m=256, tile_n=128, split_k=1))
+    r = check_sampled(p, options=dict(tile_m=256, tile_n=128, split_k=1))
     assert r["ok"], r
 
 
@@ -729,3 +729,39 @@ def test_unaligned_copy_with_a_small_workspace_falls_back():
     r, _, _ = check_full(p, workspace=small)
     assert r["ok"], r
 
+
+
+# ---------------------------------------------------------------- the boundary's own entry point
+
+@pytest.mark.parametrize("dtype,trans,shape,epi", [
+    (F16, NN, (520, 264, 1000), None),
+    (BF16, NT, (300, 520, 136), "leaky_relu"),
+    (F32, TN, (136, 200, 264), "leaky_relu"),
+    (F16, NN, (2048, 128, 2048), None),   # skinny, split K: the library's own workspace
+])
+def test_raw_tg_gemm_symbol(dtype, trans, shape, epi):
+    """Full products through the exported tg_gemm symbol itself (the
+    spec signature: sizes, pointers, leading dimensions, dtype, trans,
+    epilogue, stream), called through ctypes with device pointers."""
+    import ctypes
+    import torch
+    import tiled_gemm_02_amd as tg
+    from tests.gpu_helpers import from_device, oracle_full, torch_dtype
+    import oracle
+    M, N, K = shape
+    _say("case raw tg_gemm", dtype, trans, shape, epi)
+    p = make_problem(M, N, K, dtype, trans, "normal", seed=44)
+    A = to_device(p.A, dtype)
+    B = to_device(p.B, dtype)
+    C = torch.full((M, N), float("nan"), dtype=torch_dtype(dtype), device="cuda:0")
+    e = tg.Epilogue(tg.TG_EPI_LEAKY_RELU, 0.01, 0, 1.0, 0.0) if epi else None
+    lib = tg.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = lib.tg_gemm(M, N, K, A.data_ptr(), p.lda, B.data_ptr(), p.ldb, C.data_ptr(), N,
+                     dtype, trans, ctypes.pointer(e) if e else None, stream)
+    assert rc == tg.TG_OK, tg.tg_last_error()
+    torch.cuda.synchronize()
+    got = from_device(C, dtype)
+    ref, absab = oracle_full(p, epi)
+    r = oracle.check(got, ref, absab, dtype)
+    assert r["ok"], r

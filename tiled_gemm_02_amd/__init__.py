@@ -220,6 +220,10 @@ def _torch_dtype_code(t) -> int:
 
 
 def _ld(t) -> int:
+    """Leading dimension (row stride, elements) of a row-major 2-D tensor.
+
+    Rows must not overlap: a row stride below the row width (an expanded or
+    overlapping view) is refused, since the kernels address row r at r * ld."""
     if t.dim() != 2:
         raise ValueError("operands must be 2-D")
     rows, cols = t.shape
@@ -227,7 +231,21 @@ def _ld(t) -> int:
         return max(cols, 1)   # no element is addressed; any ld >= the width is valid
     if cols > 1 and t.stride(1) != 1:
         raise ValueError("operands must be row-major (last stride 1); pass a transpose flag instead")
-    return max(int(t.stride(0)) if rows > 1 else cols, cols, 1)
+    if rows == 1:
+        return max(cols, 1)
+    ld = int(t.stride(0))
+    if ld < cols:
+        raise ValueError(f"row stride {ld} is below the row width {cols}: rows overlap "
+                         "(expanded or overlapping views are not supported; make the tensor contiguous)")
+    return ld
+
+
+def _require_cuda(*tensors) -> None:
+    """The library reads and writes device memory only: refuse host tensors
+    before any pointer reaches a kernel."""
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise TypeError(f"expected a CUDA (device) tensor, got one on {t.device}")
 
 
 def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, out=None,
@@ -242,6 +260,7 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, o
     import torch
     if A.dtype != B.dtype:
         raise TypeError("A and B must share a dtype")
+    _require_cuda(A, B, out, workspace)
     dtype = _torch_dtype_code(A)
     M, K = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
     Kb, N = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
@@ -254,6 +273,7 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, o
     elif out.shape != (M, N) or out.dtype != A.dtype:
         raise ValueError("out has the wrong shape or dtype")
     trans = (TG_TRANS_A if trans_a else 0) | (TG_TRANS_B if trans_b else 0)
+    lda, ldb, ldc = _ld(A), _ld(B), _ld(out)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     ws_ptr, ws_bytes = (None, 0)
@@ -262,8 +282,8 @@ def gemm(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=None, o
     if M == 0 or N == 0:
         return out
     epi = _epi(epilogue, alpha, beta)
-    rc = load().tg_gemm_ex(M, N, K, A.data_ptr() if A.numel() else None, _ld(A),
-                           B.data_ptr() if B.numel() else None, _ld(B), out.data_ptr(), _ld(out),
+    rc = load().tg_gemm_ex(M, N, K, A.data_ptr() if A.numel() else None, lda,
+                           B.data_ptr() if B.numel() else None, ldb, out.data_ptr(), ldc,
                            dtype, trans, epi, _opts(options), ws_ptr, ws_bytes, stream)
     _check(rc)
     return out
@@ -276,17 +296,19 @@ def softmax(X, *, out=None, stream=None):
     import torch
     if X.dim() != 2:
         raise ValueError("X must be 2-D")
+    _require_cuda(X, out)
     dtype = _torch_dtype_code(X)
     M, N = X.shape
     if out is None:
         out = torch.empty((M, N), dtype=X.dtype, device=X.device)
     elif out.shape != X.shape or out.dtype != X.dtype:
         raise ValueError("out has the wrong shape or dtype")
+    ldx, ldy = _ld(X), _ld(out)
     if M == 0 or N == 0:
         return out
     if stream is None:
         stream = torch.cuda.current_stream(X.device).cuda_stream
-    _check(load().tg_softmax(M, N, X.data_ptr(), _ld(X), out.data_ptr(), _ld(out), dtype, stream))
+    _check(load().tg_softmax(M, N, X.data_ptr(), ldx, out.data_ptr(), ldy, dtype, stream))
     return out
 
 
@@ -301,6 +323,7 @@ def set_workspace(buf) -> None:
         tg_set_workspace(None, 0)
         _ws_keep.buf = None
         return
+    _require_cuda(buf)
     tg_set_workspace(buf.data_ptr(), buf.numel() * buf.element_size())
     _ws_keep.buf = buf
 
@@ -332,11 +355,18 @@ def autotune(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=Non
     (options for ``gemm``, mean microseconds of the fastest).  ``out`` (or a
     scratch tensor) is overwritten."""
     import torch
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must share a dtype")
+    _require_cuda(A, B, out, workspace)
     dtype = _torch_dtype_code(A)
     M, K = (A.shape[1], A.shape[0]) if trans_a else (A.shape[0], A.shape[1])
-    N = B.shape[0] if trans_b else B.shape[1]
+    Kb, N = (B.shape[1], B.shape[0]) if trans_b else (B.shape[0], B.shape[1])
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
     if out is None:
         out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    elif out.shape != (M, N) or out.dtype != A.dtype:
+        raise ValueError("out has the wrong shape or dtype")
     trans = (TG_TRANS_A if trans_a else 0) | (TG_TRANS_B if trans_b else 0)
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream

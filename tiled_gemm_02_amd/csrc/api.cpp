@@ -60,33 +60,22 @@ int mfma2_occupancy(int dtype, int trans, int bm, int bn)
     return 0;
 }
 
-// Kernel generation for 16-bit aligned operands: 2 = LDS-DMA pipeline
-// (default), 1 = register-staged kernel.  TG_MFMA_VARIANT overrides it, for
-// side-by-side timing.
-static int mfma_variant()
-{
-    static int v = [] {
-        const char *e = getenv("TG_MFMA_VARIANT");
-        return (e && e[0] == '1') ? 1 : 2;
-    }();
-    return v;
-}
-
-// The LDS-DMA kernel addresses each lane's copy with a 32-bit byte offset from
-// a per-tile 64-bit base: at most 256 rows (or 64 K-rows) of one operand, so a
-// leading dimension up to 2^22 elements keeps every offset below 2^31.
-// float32: only the 256 x 256 tile, with K-contiguous A and B, has such a kernel
-// (its leading dimensions count 16-bit units: at most 2^21 float32 elements).
+// Which macro-tile kernel family runs a vector-load plan.  16-bit operands
+// always take the LDS-DMA kernels (the planner sends leading dimensions above
+// kDmaMaxLd16 through aligned copies or element-wise loads instead).  float32
+// takes them for the 256 x 256 tile with K-contiguous A and B only (its
+// leading dimensions count 16-bit units there: at most 2^21 float32 elements);
+// its other tiles are the register-staged kernel.
 static bool use_mfma2(int dtype, int trans, bool vec, int bm, int bn, int64_t lda, int64_t ldb)
 {
-    const int64_t lim = (int64_t(1) << 23) / elem_bytes(dtype);
-    if (!vec || lda > lim || ldb > lim)
+    if (!vec)
         return false;
     if (dtype == TG_F32)
-        return bm == 256 && bn == 256 && trans == TG_NT;
-    if (bm == 192)
-        return true;   // the 192 x 256 tile exists on the ping-pong kernel only
-    return mfma_variant() == 2;
+        return bm == 256 && bn == 256 && trans == TG_NT && lda <= kDmaMaxLd16 / 2 &&
+               ldb <= kDmaMaxLd16 / 2;
+    (void)lda;
+    (void)ldb;
+    return true;
 }
 
 int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec)
@@ -463,6 +452,8 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         kps = (kps + BK - 1) / BK * BK;
         a.kps = (int)kps;
         a.splits = pl.split_k;
+        if (pl.vector_io != 0 && p.dtype != TG_F32 && (p.lda > kDmaMaxLd16 || p.ldb > kDmaMaxLd16))
+            return fail(TG_ERR_UNSUPPORTED, "16-bit vector-load plan with a leading dimension above 2^22");
         if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, pl.tile_m, pl.tile_n, p.lda, p.ldb))
             e = launch_mfma2(p.dtype, p.trans, pl.tile_m, pl.tile_n, a, s);
         else

@@ -2,7 +2,9 @@
 #include <algorithm>
 #define TG_TRAIT BF16
 #define TG_NAME bf16
-#define TG_TILE_LIST TG_TILE(256, 256) TG_TILE(256, 128) TG_TILE(128, 128) TG_TILE(128, 64) TG_TILE(64, 64)
+// 16-bit vector loads run on the LDS-DMA kernels only: the register-staged
+// kernel keeps its element-wise 64 x 64 form for operands off the 16-byte grid
+#define TG_TILE_LIST
 #define TG_HAS_MFMA2 1
 #define TG_HAS_SKINNY 1
 #include "instances.inc"

@@ -116,9 +116,16 @@ static void fill_common(const Problem &p, const Chip &chip, tg_plan *out)
     out->arith_intensity = bytes > 0 ? 2.0 * p.M * p.N * p.K / bytes : 0.0;
 }
 
+// Operands the 128-bit-load kernels take as they lie: sizes, leading
+// dimensions and base pointers on the 16-byte grid.  16-bit operands then run
+// on the LDS-DMA kernels, which address a tile's rows by 32-bit byte offsets
+// from a per-tile base: leading dimensions up to kDmaMaxLd16 elements.  Wider
+// rows are read through aligned copies (or element-wise loads).
 static bool vec_ok(const Problem &p)
 {
     const int E = chunk_elems(p.dtype);
+    if (p.dtype != TG_F32 && (p.lda > kDmaMaxLd16 || p.ldb > kDmaMaxLd16))
+        return false;
     return p.ptrs_aligned && p.M % E == 0 && p.N % E == 0 && p.K % E == 0 && p.lda % E == 0 &&
            p.ldb % E == 0;
 }

@@ -93,6 +93,10 @@ struct PackLayout {
 PackLayout pack_layout(const Problem &p, bool nt = false);
 Problem packed_problem(const Problem &p, bool nt = false);
 
+// Widest leading dimension (elements) of a 16-bit operand the LDS-DMA
+// kernels read in place: a tile's 256 rows then span less than 2^31 bytes.
+constexpr int64_t kDmaMaxLd16 = (int64_t)1 << 22;
+
 // 16-byte-chunk element count of a storage type.
 inline int chunk_elems(int dtype) { return dtype == TG_F32 ? 4 : 8; }
 inline int elem_bytes(int dtype) { return dtype == TG_F32 ? 4 : 2; }
