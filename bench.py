@@ -32,6 +32,48 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s + % MFMA peak (fp16 8192³); GB/s + % HBM peak (8192×128×8192)"
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# The pages' own arithmetic-intensity figures ("Matrix Multiplication
+# Background User's Guide", section 2), quoted with the hardware they are
+# stated for, beside this chip's ridge point (dense matrix peak / HBM rate).
+PAGES_CONTEXT = {
+    "v100_fp16_tensor_core_ops_per_byte": 138.9,
+    "ai_8192x128x8192_fp16_flop_per_byte": 124.1,
+    "ai_8192x8192x8192_fp16_flop_per_byte": 2730,
+    "ai_gemv_flop_per_byte": "< 1",
+    "hardware_of_those_figures": "NVIDIA V100 (the guide's example)",
+}
+
+
+def ridge(dtype_name: str) -> float:
+    """FLOP per byte at which the dense matrix peak and HBM bandwidth meet on MI355X."""
+    return PEAK_TFLOPS[dtype_name] * 1e12 / (PEAK_HBM_GBS * 1e9)
+
+
+def bound_of(M: int, N: int, K: int, dtype_code: int) -> str:
+    """'hbm' when the algorithmic arithmetic intensity 2MNK / s(MK + KN + MN)
+    is below the chip's ridge for that type, else 'mfma' (the guide's
+    section 2 test, with MI355X's figures)."""
+    from gemm_inputs import DTYPE_NAMES, ELEM_BYTES
+    s = ELEM_BYTES[dtype_code]
+    ai = 2.0 * M * N * K / (s * (M * K + K * N + M * N))
+    return "hbm" if ai < ridge(DTYPE_NAMES[dtype_code]) else "mfma"
+
+
+def host_cpu() -> dict:
+    """CPUs this process may run on, the machine's logical CPU count and the CPU model."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"usable_cpus": usable, "nproc": os.cpu_count(), "cpu_model": model}
 ROTATE_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _K = "tiled_gemm_02_amd/csrc/kernels/"
@@ -227,9 +269,12 @@ def cpu_baseline(name: str, target_s: float):
     rows = int(max(1, min(p.M, target_s / max(t1, 1e-6))))
     t = run(rows)
     macs = rows * p.N * p.K
+    hc = host_cpu()
     return {"value": 2.0 * macs / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_usable_cpus": hc["usable_cpus"], "host_nproc": hc["nproc"], "cpu_model": hc["cpu_model"],
             "sample": f"{rows} full output rows ({rows}x{p.N} elements, {macs / 1e9:.1f} G multiply-adds) "
-                      f"of the {p.M}x{p.N}x{p.K} {name} workload, fp64 triple loop, {t:.1f} s"}
+                      f"of the {p.M}x{p.N}x{p.K} {name} workload, fp64 triple loop on {threads} threads, "
+                      f"{t:.1f} s"}
 
 
 def roofline_entry(r, bound):
@@ -354,6 +399,54 @@ def traffic_summarize(root: str):
 
 
 # ---------------------------------------------------------------- quantization sweep
+
+def sweep_summary(device, step: int = 64, reps: int = 5) -> dict:
+    """The tile/wave-quantization sweep at a coarse step for the benchmark line:
+    fp16 M = 2304, K = 4096, N = 1536 .. 6144 every `step` columns, the
+    planner's plan, inputs N(0,1)/sqrt(K) from a seeded device generator (B is
+    the first N columns of one 4096 x 6144 draw, made contiguous).  Each point
+    is the median of `reps` event-timed calls after two warm-ups, with one
+    persistent workspace; reported as TFLOP/s over the points."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    from gemm_inputs import sweep_ns
+    M, K = 2304, 4096
+    g = torch.Generator(device=device).manual_seed(0)
+    A = (torch.randn((M, K), generator=g, device=device) / math.sqrt(K)).half()
+    Bfull = (torch.randn((K, 6144), generator=g, device=device) / math.sqrt(K)).half()
+    stream = torch.cuda.current_stream(device)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=device)
+    pts = []
+    for N in sweep_ns(step=step):
+        B = Bfull[:, :N].contiguous()
+        C = torch.empty((M, N), dtype=torch.float16, device=device)
+        for _ in range(2):
+            tg.gemm(A, B, out=C, workspace=ws, stream=stream.cuda_stream)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            tg.gemm(A, B, out=C, workspace=ws, stream=stream.cuda_stream)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = sorted(ts)[len(ts) // 2]
+        pl = tg.tg_gemm_plan(M, N, K, tg.TG_F16, tg.TG_NN)
+        pts.append((N, 2.0 * M * N * K / ms / 1e9, pl))
+    tf = sorted(v for _, v, _ in pts)
+    low = sorted(v for n, v, _ in pts if n <= 1792)
+    mean = sum(tf) / len(tf)
+    peak = PEAK_TFLOPS["f16"]
+    return {"workload": "sweep_2304xNx4096_f16", "unit": "TFLOP/s", "points": len(pts), "step": step,
+            "n_range": [pts[0][0], pts[-1][0]],
+            "value": round(mean, 2), "mean": round(mean, 2), "median": round(tf[len(tf) // 2], 2),
+            "min": round(tf[0], 2), "max": round(tf[-1], 2),
+            "median_n_le_1792": round(low[len(low) // 2], 2) if low else None,
+            "per_point": [[n, round(v, 1), f"{pl['tile_m']}x{pl['tile_n']}", pl["split_k"], pl["tiles"]]
+                          for n, v, pl in pts],
+            "roofline": {"bound": "mfma", "achieved": round(mean, 2), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(mean / peak, 4), "traffic": None}}
+
 
 def sweep(out_path: str, step: int, reps: int = 5, tune: bool = False):
     """fp16 M=2304, K=4096, N = 1536 .. 6144: the planner's tile against a fixed 256 x 256 one.
@@ -624,8 +717,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="f16_8192")
     ap.add_argument("--secondary", default="f16_skinny_8192x128x8192,f16_gemv_1x8192x8192,"
-                    "softmax_f32_4096x32768,softmax_f16_4096x32768,f16_4096_nt,f32_8192_nt",
-                    help="comma-separated workloads reported alongside ('' for none)")
+                    "f16_4096_nt,bf16_leaky_8192,bf16_leaky_6912x2048x4096,f32_256,sweep,"
+                    "softmax_f32_4096x32768,softmax_f16_4096x32768,f32_8192_nt",
+                    help="comma-separated workloads reported alongside ('' for none); 'sweep' is "
+                         "the M=2304, K=4096 N-sweep at step 64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--sweep", default=None,
@@ -680,7 +775,7 @@ def main():
     log("device", torch.cuda.get_device_name(0), "cus", tg.tg_device_cus())
 
     w = WORKLOADS[args.workload]
-    mem_bound = w["N"] <= 256 or w["M"] == 1
+    mem_bound = bound_of(w["M"], w["N"], w["K"], w["dtype"]) == "hbm"
     log("timing", args.workload)
     r = time_workload(args.workload, args.steps, args.warmup, device, rotate=mem_bound)
     d = r["d"]
@@ -710,10 +805,17 @@ def main():
                                                   "tiles", "waves", "occupancy")}},
         "ms_median": round(r["ms_median"], 5),
         "roofline": roofline_entry(r, "hbm" if mem_bound else "mfma"),
+        "context": dict(PAGES_CONTEXT, mi355x_ridge_fp16_flop_per_byte=round(ridge("f16"), 1),
+                        mi355x_ridge_fp32_flop_per_byte=round(ridge("f32"), 1),
+                        workload_ai_flop_per_byte=round(r["plan"]["arith_intensity"], 1)),
     }
     sec = []
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
         log("timing", name)
+        if name == "sweep":
+            sec.append(sweep_summary(device))
+            torch.cuda.empty_cache()
+            continue
         if name.startswith("softmax_"):
             rs = time_softmax(name, max(args.steps, 50), args.warmup, device)
             ent = roofline_entry(rs, "hbm")
@@ -727,13 +829,19 @@ def main():
             torch.cuda.empty_cache()
             continue
         ws = WORKLOADS[name]
-        sec_mem = ws["N"] <= 256 or ws["M"] == 1
+        sec_mem = bound_of(ws["M"], ws["N"], ws["K"], ws["dtype"]) == "hbm"
         rs = time_workload(name, max(args.steps, 50), args.warmup, device, rotate=sec_mem)
         ent = roofline_entry(rs, "hbm" if sec_mem else "mfma")
+        p = rs["p"]
         sec.append({"workload": name, "value": ent["achieved"], "unit": ent["unit"],
                     "ms_per_step": round(rs["ms_per_step"], 5),
+                    "us_per_step": round(rs["ms_per_step"] * 1e3, 2),
+                    "config": {"M": p.M, "N": p.N, "K": p.K, "dtype": rs["d"]["dtype"],
+                               "layout": ["NN", "TN", "NT", "TT"][p.trans],
+                               "epilogue": rs["d"]["epi"] or "none",
+                               "ai_flop_per_byte": round(rs["plan"]["arith_intensity"], 1)},
                     "plan": {k: rs["plan"][k] for k in ("path_name", "tile_m", "tile_n", "split_k",
-                                                         "workgroups")},
+                                                         "tiles", "workgroups", "waves")},
                     "roofline": ent, "rotated_copies": rs["d"]["copies"]})
         del rs
         torch.cuda.empty_cache()

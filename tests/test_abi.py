@@ -117,3 +117,26 @@ def test_set_workspace_argument_checks():
     with pytest.raises(tg.TgError):
         tg.tg_set_workspace(0x1000 + 16, 1024)
     assert tg.tg_set_workspace(None, 0) == 0
+
+
+def _kernel_stubs():
+    """Demangled names of the kernel launch stubs the library holds (host side)."""
+    import subprocess
+    out = subprocess.run(["nm", "-C", tg.LIB_PATH], check=True, capture_output=True, text=True).stdout
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["F16", "BF16"])
+def test_every_planned_16bit_tile_has_kernels(dtype):
+    """Every macro tile the planner may pick for 16-bit operands has its kernel
+    compiled for all four layouts (256 x 256 and 192 x 256: the ping-pong
+    kernel; the others: the four-wave LDS-DMA kernel), so no plan can reach a
+    launcher without an instance."""
+    import re
+    stubs = _kernel_stubs()
+    for bm, bn in [(256, 128), (128, 128), (128, 64), (64, 64)]:
+        found = set(re.findall(rf"tg::mfma_gemm3_kernel<tg::{dtype}, {bm}, {bn}, \d+, 2, 2, (\w+), (\w+)>", stubs))
+        assert len(found) == 4, (bm, bn, found)
+    for bm in (256, 192):
+        found = set(re.findall(rf"tg::mfma_pingpong_kernel<tg::{dtype}, \d, 16, (\w+), (\w+), false, {bm}>", stubs))
+        assert len(found) == (4 if bm == 256 else 2), (bm, found)

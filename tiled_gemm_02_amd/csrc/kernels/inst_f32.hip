@@ -2,7 +2,7 @@
 #include <algorithm>
 #define TG_TRAIT F32
 #define TG_NAME f32
-#define TG_TILE_LIST TG_TILE(128, 128) TG_TILE(64, 64)
+#define TG_REG_TILE_LIST TG_TILE(128, 128) TG_TILE(64, 64)
 #define TG_HAS_MFMA2 0
 #define TG_HAS_PP_NT 1     // the ping-pong kernel, K-contiguous operands
 #define TG_HAS_SKINNY 0
