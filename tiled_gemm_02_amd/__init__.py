@@ -73,6 +73,15 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m tiled_gemm_02_amd.build`")
+    # PyTorch ships its own HIP runtime under the same soname as the system's.
+    # Imported first, it is the runtime this library binds to, so torch's
+    # allocations, streams and graph captures and this library's launches share
+    # one runtime.  Loaded the other way round, the process would hold two
+    # runtimes and torch would find no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the library also runs without torch
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     ep, op, pp = ctypes.POINTER(Epilogue), ctypes.POINTER(Options), ctypes.POINTER(Plan)
