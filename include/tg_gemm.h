@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 105
+#define TG_VERSION 106
 
 /* storage type of A, B and C */
 enum tg_dtype { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 };
@@ -184,6 +184,32 @@ int tg_gemm_ex(int64_t M, int64_t N, int64_t K,
                const tg_options *opts,
                void *workspace, size_t workspace_bytes,
                void *stream);
+
+/* Size of the static scratch of tg_gemm_noalloc: 64 MiB per device. */
+#define TG_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* tg_gemm_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the call allocates nothing, with any allocator, and never uses the thread's
+ * default workspace.  Whatever workspace the plan needs (float32 K-split
+ * partials, stream-K pieces, aligned operand copies) comes from a scratch
+ * array of TG_NOALLOC_SCRATCH_BYTES that the library holds in device memory on
+ * every device it runs on, from the first call on that device until the
+ * process ends.  An unforced plan that would need more is replaced as for a
+ * small tg_gemm_ex workspace (no K split, then no copies); a forced K split
+ * or stream-K that needs more is refused with TG_ERR_ARG, naming the maximum.
+ * Every call on a device shares that device's scratch, and each call rewrites
+ * whatever of it it reads: calls that may overlap on one device (several
+ * streams, several host threads) race, and must be ordered by the caller.
+ * Arguments and results as tg_gemm_ex. */
+int tg_gemm_noalloc(int64_t M, int64_t N, int64_t K,
+                    const void *A, int64_t lda,
+                    const void *B, int64_t ldb,
+                    void *C, int64_t ldc,
+                    int dtype, int trans,
+                    const tg_epilogue *epilogue,
+                    const tg_options *opts,
+                    void *stream);
 
 /* The plan tg_gemm_ex would run on the current device (no launch). */
 int tg_gemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int trans,

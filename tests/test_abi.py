@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert tg.tg_version() == 105
+    assert tg.tg_version() == 106
 
 
 def test_epilogue_struct_matches_header(tmp_path):

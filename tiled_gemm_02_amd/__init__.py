@@ -93,6 +93,8 @@ def load():
     lib.tg_autotune.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, i32, ep, vp,
                                 ctypes.c_size_t, vp, i32, op, ctypes.POINTER(ctypes.c_float)]
     lib.tg_autotune.restype = i32
+    lib.tg_gemm_noalloc.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, i32, i32, ep, op, vp]
+    lib.tg_gemm_noalloc.restype = i32
     lib.tg_gemm_plan.argtypes = [i64, i64, i64, i32, i32, op, pp]
     lib.tg_gemm_plan.restype = i32
     lib.tg_plan_model.argtypes = [i64, i64, i64, i32, i32, i32, i32, op, pp]
@@ -179,6 +181,14 @@ def tg_gemm_ex(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue=None, opt
                workspace=None, workspace_bytes=0, stream=None) -> int:
     return load().tg_gemm_ex(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, _epi(epilogue),
                              _opts(options), workspace, workspace_bytes, stream)
+
+
+def tg_gemm_noalloc(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue=None, options=None,
+                    stream=None) -> int:
+    """Raw call of the entry point that allocates nothing (its workspace is the
+    library's static scratch); returns the status (does not raise)."""
+    return load().tg_gemm_noalloc(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, _epi(epilogue),
+                                  _opts(options), stream)
 
 
 def tg_gemm_plan(M, N, K, dtype, trans=TG_NN, options=None) -> dict:

@@ -211,6 +211,9 @@ struct DeviceInfo {
     // mapping tens of MiB again costs more than the split or copy it serves)
     hipMemPool_t pool = nullptr;
     bool pool_tried = false;
+    // device address of this device's copy of `scratch` (tg_gemm_noalloc),
+    // taken once with this device current; null until then
+    void *scratch_ptr = nullptr;
     // measured residency per (dtype, trans, tile, vec), 0 = not yet asked
     int occ[3][4][8][2] = {};
     // benchmark-mode winners (tg_autotune) per problem, used by calls that
@@ -219,6 +222,13 @@ struct DeviceInfo {
 };
 
 static std::mutex g_tune_mu;
+
+// Scratch of tg_gemm_noalloc: K-split partials, stream-K pieces and aligned
+// operand copies, for callers that cannot allocate.  Every device the library
+// runs on holds its own copy for the life of the process.  Host code never
+// uses the name itself (on the host it is only a stand-in for the symbol):
+// kernels get the device address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[TG_NOALLOC_SCRATCH_BYTES];
 
 // The cached benchmark-mode winner for p, if there is one.
 static bool tune_lookup(DeviceInfo *dev, const Problem &p, tg_options *out)
@@ -536,12 +546,30 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
 static thread_local void *t_ws = nullptr;
 static thread_local size_t t_ws_bytes = 0;
 
+// The device address of the current device's `scratch` array, taken on the
+// first request with that device current and kept per device.
+static int scratch_address(DeviceInfo *dev, void **out)
+{
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (!dev->scratch_ptr) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(TG_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        dev->scratch_ptr = ptr;
+    }
+    *out = dev->scratch_ptr;
+    return TG_OK;
+}
+
+// static_scratch: workspace is this device's `scratch` array (tg_gemm_noalloc);
+// nothing is allocated, and a forced plan that needs more is refused.
 static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
                      int64_t ldb, void *C, int64_t ldc, int dtype, int trans,
                      const tg_epilogue *epi, const tg_options *opts, void *user_ws,
-                     size_t user_ws_bytes, void *stream)
+                     size_t user_ws_bytes, void *stream, bool static_scratch = false)
 {
-    if (!user_ws) {
+    if (!user_ws && !static_scratch) {
         user_ws = t_ws;
         user_ws_bytes = t_ws_bytes;
     }
@@ -554,6 +582,12 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
     rc = current_device(&dev);
     if (rc != TG_OK)
         return rc;
+    if (static_scratch) {
+        rc = scratch_address(dev, &user_ws);
+        if (rc != TG_OK)
+            return rc;
+        user_ws_bytes = TG_NOALLOC_SCRATCH_BYTES;
+    }
     hipStream_t s = (hipStream_t)stream;
     const OutEpi oe0 = out_epi(epi);
     if (K == 0 || oe0.alpha == 0.0f) {
@@ -597,9 +631,16 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
             ws = nullptr;
         }
         if (!ws) {
-            if (opts && (opts->split_k > 1 || opts->split_k == TG_SPLIT_STREAM_K) && !from_cache)
+            if (opts && (opts->split_k > 1 || opts->split_k == TG_SPLIT_STREAM_K) && !from_cache) {
+                if (static_scratch)
+                    return fail(TG_ERR_ARG,
+                                "forced split_k=%d needs %llu bytes of scratch; the static scratch "
+                                "holds %llu (TG_NOALLOC_SCRATCH_BYTES)",
+                                opts->split_k, (unsigned long long)pl.workspace_bytes,
+                                (unsigned long long)TG_NOALLOC_SCRATCH_BYTES);
                 return fail(TG_ERR_ARG, "forced split_k=%d needs %llu bytes of workspace",
                             opts->split_k, (unsigned long long)pl.workspace_bytes);
+            }
             // without the room: no K split, then no aligned copies either
             tg_options o = opts ? *opts : tg_options{TG_PATH_AUTO, 0, 0, 0};
             o.split_k = 1;
@@ -683,6 +724,14 @@ int tg_gemm_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, cons
 {
     return gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue, opts, workspace,
                      workspace_bytes, stream);
+}
+
+int tg_gemm_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                    int64_t ldb, void *C, int64_t ldc, int dtype, int trans,
+                    const tg_epilogue *epilogue, const tg_options *opts, void *stream)
+{
+    return gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, dtype, trans, epilogue, opts, nullptr, 0,
+                     stream, true);
 }
 
 int tg_gemm_plan(int64_t M, int64_t N, int64_t K, int dtype, int trans, const tg_options *opts,
