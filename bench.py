@@ -303,7 +303,8 @@ def roofline_entry(r, bound):
 # changed kernel reports null until it is measured again.
 
 TRAFFIC_WORKLOADS = ["f16_8192", "f16_skinny_8192x128x8192", "f16_gemv_1x8192x8192",
-                     "softmax_f32_4096x32768", "softmax_f16_4096x32768", "f16_4096_nt", "f32_8192_nt"]
+                     "softmax_f32_4096x32768", "softmax_f16_4096x32768", "f16_4096_nt", "f32_8192_nt",
+                     "bf16_leaky_8192", "bf16_leaky_6912x2048x4096", "f32_256"]
 COPY_BYTES = 256 << 20
 DOMINANT = {"mfma": "mfma_", "skinny": "skinny_kernel", "softmax": "softmax_rows_kernel"}
 # GEMV: gemv_cols / gemv_rows
@@ -325,7 +326,7 @@ def traffic_kernel(name: str, launches: int = 6):
         return
     from gemm_inputs import WORKLOADS
     w = WORKLOADS[name]
-    time_workload(name, launches, 1, device, rotate=w["N"] <= 256 or w["M"] == 1)
+    time_workload(name, launches, 1, device, rotate=bound_of(w["M"], w["N"], w["K"], w["dtype"]) == "hbm")
 
 
 def _counter_avg(csv_path: str, sub: str, counter: str):
@@ -396,6 +397,98 @@ def traffic_summarize(root: str):
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
     open(os.path.join(ROOT, "profiles", "traffic_summary.md"), "w").write("\n".join(lines))
     print("\n".join(lines))
+
+
+# ---------------------------------------------------------------- kernel-time summary
+#
+# `rocprofv3 --kernel-trace --stats -d DIR -o run --output-format csv -- python3 bench.py ...`
+# with the bench's own JSON line saved as DIR/bench.json; `--kernel-stats-summarize DIR OUT`
+# groups the library's dispatches by (kernel, workgroup grid), which tells the workloads
+# apart even where two of them run the same kernel, and sets each line's step time beside
+# its dominant kernel's average from the same run.
+
+def _dominant_match(line, name, wgx, wgy):
+    """Whether a dispatch of `name` on a (wgx, wgy) workgroup grid is the dominant kernel of
+    the bench line `line` (headline or secondary dict)."""
+    plan = line.get("plan") or line.get("config", {}).get("plan") or {}
+    cfg = line.get("config", {})
+    dt = {"f16": "F16", "bf16": "BF16", "f32": "F32"}.get(cfg.get("dtype") or line.get("dtype"), "")
+    wl = line.get("workload") or cfg.get("workload", "")
+    if wl.startswith("softmax_"):
+        return "softmax_rows_kernel" in name and f"<tg::{dt}," in name
+    path = plan.get("path_name")
+    if path == "mfma":
+        return (name.startswith("void tg::mfma_") and f"<tg::{dt}," in name and wgx == plan.get("tiles")
+                and wgy == max(1, plan.get("split_k", 1)))
+    if path == "skinny":
+        return "skinny_kernel" in name and f"<tg::{dt}," in name and wgx == plan.get("tiles") and \
+            wgy == max(1, plan.get("split_k", 1))
+    if path == "gemv":
+        return "gemv_" in name and "reduce" not in name and f"<tg::{dt}," in name
+    return False
+
+
+def kernel_stats_summarize(root: str, out_path: str):
+    import csv
+    import glob
+    trace = glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)
+    if not trace:
+        raise SystemExit(f"no kernel_trace.csv under {root}")
+    line = json.loads(open(os.path.join(root, "bench.json")).read().strip().splitlines()[-1])
+    groups = {}
+    for r in csv.DictReader(open(trace[0])):
+        name = r["Kernel_Name"]
+        if "tg::" not in name:
+            continue
+        wgx = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        wgy = int(r["Grid_Size_Y"]) // max(1, int(r["Workgroup_Size_Y"]))
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((name, wgx, wgy), []).append(us)
+    total = sum(sum(v) for v in groups.values())
+    lines = [line] + [dict(sc) for sc in line.get("secondary", [])]
+    out = ["# Kernel time summary of the default benchmark command", "",
+           "Command (repository root, one MI355X; the bench's own JSON line from the same run goes",
+           "to bench.json):", "", "```",
+           f"rocprofv3 --kernel-trace --stats -d {root} -o run --output-format csv -- "
+           f"python3 bench.py {line.get('bench_args', '')}".rstrip() + f" > {root}/bench.json",
+           f"python3 bench.py --kernel-stats-summarize {root} {out_path}", "```", "",
+           "Dispatches are grouped by kernel and workgroup grid (x tiles, y K splits), which tells",
+           "the workloads apart where two of them run the same kernel.  Each line's step time is",
+           "the bench's own HIP-event figure from the profiled run (kernel tracing serialises the",
+           "launches, so profiled steps run somewhat longer than unprofiled ones); a step holds the",
+           "dominant kernel and, where the plan splits K, the reduction, so the kernel average must",
+           "not exceed it.  Calls / Avg / Min / Max cover the launches of the timed region only (the",
+           "warm-up launches, the first of them cold, are left out); the table of all kernels below",
+           "counts every launch.", "",
+           "| Bench line | Step (us) | Dominant kernel | Grid | Calls | Avg (us) | Min (us) | Max (us) | Avg <= step |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for ln in lines:
+        wl = ln.get("workload") or ln.get("config", {}).get("workload")
+        if wl is None or wl.startswith("sweep"):
+            continue
+        step_us = ln["ms_per_step"] * 1e3
+        hit = [(k, v) for k, v in groups.items() if _dominant_match(ln, *k)]
+        if not hit:
+            out.append(f"| {wl} | {step_us:.1f} | (no matching dispatch) | | | | | | |")
+            continue
+        (name, gx, gy), v = max(hit, key=lambda kv: len(kv[1]))
+        # the launches of the timed region: the last `steps` of the group (the
+        # warm-up launches come first, the coldest among them)
+        n_timed = ln.get("steps") or max(int(line.get("steps", 50)), 50)
+        v = v[-n_timed:]
+        avg = sum(v) / len(v)
+        short = name.replace("void tg::", "").split("(")[0]
+        out.append(f"| {wl} | {step_us:.1f} | `{short}` | {gx} x {gy} | {len(v)} | {avg:.1f} | {min(v):.1f} | "
+                   f"{max(v):.1f} | {'yes' if avg <= step_us else 'NO'} |")
+    out += ["", "All library kernels of the run:", "",
+            "| Kernel | Grid | Calls | Avg (us) | Min (us) | Max (us) | Share |", "|---|---|---|---|---|---|---|"]
+    for (name, gx, gy), v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:40]:
+        short = name.replace("void tg::", "").split("(")[0]
+        out.append(f"| `{short}` | {gx} x {gy} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                   f"{100 * sum(v) / total:.1f}% |")
+    out.append("")
+    open(out_path, "w").write("\n".join(out))
+    print("\n".join(out))
 
 
 # ---------------------------------------------------------------- quantization sweep
@@ -550,7 +643,7 @@ def align_sweep(out_path: str, reps: int = 5):
     """fp16 NN products of about 4096^3 with one size off the 16-byte grid: K = 4096 + d
     (rows of A off the grid) and M = N = 4096 + d (ragged tiles and rows of B and C off
     the grid) for d = 0 .. 16 (the alignment effect of "Matrix Multiplication Background
-    User's Guide", section 3.1).  Aligned sizes take the LDS-DMA kernels directly, the
+    User's Guide", section 2.2, Figure 2).  Aligned sizes take the LDS-DMA kernels directly, the
     others aligned copies (staged in float32 when M or N is off the grid)."""
     import torch
     import tiled_gemm_02_amd as tg
@@ -738,9 +831,15 @@ def main():
                     help="run one workload (or 'copy') for a rocprofv3 counter pass, then exit")
     ap.add_argument("--traffic-summarize", default=None,
                     help="turn counter passes under this folder into the traffic table, then exit")
+    ap.add_argument("--kernel-stats-summarize", nargs=2, default=None, metavar=("DIR", "OUT"),
+                    help="turn a rocprofv3 kernel trace of a bench run (with its JSON line in DIR/bench.json) "
+                         "into the kernel-time table OUT, then exit")
     args = ap.parse_args()
     if args.traffic_summarize:
         traffic_summarize(args.traffic_summarize)
+        return
+    if args.kernel_stats_summarize:
+        kernel_stats_summarize(*args.kernel_stats_summarize)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -803,6 +902,7 @@ def main():
                    "seed": p.desc["seed"], "dist": p.desc["dist"], "plan": {
                        k: r["plan"][k] for k in ("path_name", "tile_m", "tile_n", "split_k",
                                                   "tiles", "waves", "occupancy")}},
+        "bench_args": " ".join(sys.argv[1:]),
         "ms_median": round(r["ms_median"], 5),
         "roofline": roofline_entry(r, "hbm" if mem_bound else "mfma"),
         "context": dict(PAGES_CONTEXT, mi355x_ridge_fp16_flop_per_byte=round(ridge("f16"), 1),
@@ -822,6 +922,7 @@ def main():
             p = rs["p"]
             sec.append({"workload": name, "value": ent["achieved"], "unit": "GB/s",
                         "ms_per_step": round(rs["ms_per_step"], 5),
+                        "steps": max(args.steps, 50), "warmup": args.warmup,
                         "config": {"M": p.M, "N": p.N, "dtype": rs["d"]["dtype"],
                                    "waves_per_row": rs["shape"][0], "chunks_per_lane": rs["shape"][1]},
                         "roofline": ent, "rotated_copies": rs["d"]["copies"]})
@@ -836,6 +937,7 @@ def main():
         sec.append({"workload": name, "value": ent["achieved"], "unit": ent["unit"],
                     "ms_per_step": round(rs["ms_per_step"], 5),
                     "us_per_step": round(rs["ms_per_step"] * 1e3, 2),
+                    "steps": max(args.steps, 50), "warmup": args.warmup,
                     "config": {"M": p.M, "N": p.N, "K": p.K, "dtype": rs["d"]["dtype"],
                                "layout": ["NN", "TN", "NT", "TT"][p.trans],
                                "epilogue": rs["d"]["epi"] or "none",

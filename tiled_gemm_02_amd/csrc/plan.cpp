@@ -667,8 +667,9 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
     }
     if (allow_pack && !vec_ok(p) && pack_worthwhile(p) && !(opts && opts->path == TG_PATH_GEMV)) {
         // plan the padded, aligned copy ("Matrix Multiplication Background
-        // User's Guide", section 3.1: multiples of 8 elements keep the matrix
-        // units fed; padding is how a caller gets there)
+        // User's Guide", section 2.2, Table 1 and Figure 2: 16-bit products run
+        // best with sizes that are multiples of 8 elements; padding is how a
+        // caller gets there)
         const Problem q = packed_problem(p, nt);
         const PackLayout L = pack_layout(p, nt);
         tg_plan inner;
