@@ -161,7 +161,12 @@ typedef struct tg_plan {
  * or aligned copies of A and B), it comes from the calling thread's default
  * workspace (tg_set_workspace) when one is set, else it is a stream-ordered
  * allocation on `stream` from a memory pool the library keeps per device:
- * memory a call frees stays reserved for later calls until the process ends. */
+ * memory a call frees stays reserved for later calls until the process ends,
+ * and a call that allocates cannot be recorded into a HIP graph.  (The guide
+ * says only that a K split adds a reduction over partial tiles, "Matrix
+ * Multiplication Background User's Guide", section 2.3; this call keeps the
+ * split and supplies the buffer itself.)  Callers that must not allocate use
+ * tg_gemm_ex with their own workspace, or tg_gemm_noalloc. */
 int tg_gemm(int64_t M, int64_t N, int64_t K,
             const void *A, int64_t lda,
             const void *B, int64_t ldb,
