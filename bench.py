@@ -13,6 +13,11 @@ product and the 1 x 8192 x 8192 GEMV, in GB/s of algorithmic bytes
 (A, B and C once each) against HBM bandwidth; their inputs rotate over copies
 totalling >= 512 MiB so the 256 MB Infinity Cache cannot serve them.
 
+Every timed workload first runs untimed steps back to back for a quarter
+second ("settle"), then its warm-up steps, then the timed steps: the engine
+clock ramps up from idle over tens of milliseconds of load, and a workload of
+a few milliseconds in all would otherwise be timed on the ramp.
+
 The CPU baseline is the float64 oracle, timed on a bounded sample of the
 headline workload's output rows on this host.
 """
@@ -132,6 +137,42 @@ def dev_tensor(arr, dtype_code, device):
     return torch.from_numpy(a).to(device)
 
 
+SETTLE_S = 0.25   # untimed GPU-busy seconds before a workload's warm-up steps
+
+
+def settle(step, device, seconds: float = SETTLE_S) -> int:
+    """Run untimed steps back to back until `seconds` of wall time have passed.
+
+    The engine clock ramps up from its idle level over tens of milliseconds of
+    load: after host-side input preparation (seconds of numpy) a workload whose
+    warm-up plus timed steps add up to a few milliseconds would otherwise be
+    timed at the ramp's start.  Returns the number of steps run."""
+    import torch
+    t0 = time.perf_counter()
+    n, chunk = 0, 1
+    while True:
+        for _ in range(chunk):
+            step(n)
+            n += 1
+        torch.cuda.synchronize(device)
+        if time.perf_counter() - t0 >= seconds:
+            return n
+        chunk = min(chunk * 2, 256)
+
+
+def time_back_to_back(call, stream, reps: int) -> float:
+    """Mean milliseconds of `reps` calls issued back to back between two
+    events on the launch stream."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def prepare(name: str, device, rotate: bool):
     import torch
     from gemm_inputs import DTYPE_NAMES, ELEM_BYTES, WORKLOADS, make_problem
@@ -181,6 +222,7 @@ def time_workload(name: str, steps: int, warmup: int, device, rotate: bool):
         tg.gemm(d["As"][j], d["Bs"][j], trans_a=p.trans_a, trans_b=p.trans_b, epilogue=epi,
                 out=d["C"], alpha=d["alpha"], beta=d["beta"], workspace=ws, stream=stream.cuda_stream)
 
+    n_settle = settle(step, device)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize(device)
@@ -198,7 +240,7 @@ def time_workload(name: str, steps: int, warmup: int, device, rotate: bool):
     per_sorted = sorted(per)
     return dict(name=name, p=p, d=d, ms_per_step=total_ms / steps,
                 ms_median=per_sorted[len(per_sorted) // 2], ms_min=per_sorted[0], wall_s=wall,
-                plan=plan)
+                plan=plan, settle_steps=n_settle)
 
 
 def prepare_softmax(name: str, device):
@@ -228,6 +270,7 @@ def time_softmax(name: str, steps: int, warmup: int, device):
     def step(i):
         tg.softmax(d["Xs"][i % d["copies"]], out=d["Y"], stream=stream.cuda_stream)
 
+    n_settle = settle(step, device)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize(device)
@@ -239,7 +282,7 @@ def time_softmax(name: str, steps: int, warmup: int, device):
     torch.cuda.synchronize(device)
     total_ms = evs[0].elapsed_time(evs[-1])
     q, c = tg.softmax_shape(p.N, p.dtype)
-    return dict(name=name, p=p, d=d, ms_per_step=total_ms / steps, shape=(q, c))
+    return dict(name=name, p=p, d=d, ms_per_step=total_ms / steps, shape=(q, c), settle_steps=n_settle)
 
 
 def cpu_baseline(name: str, target_s: float):
@@ -493,13 +536,15 @@ def kernel_stats_summarize(root: str, out_path: str):
 
 # ---------------------------------------------------------------- quantization sweep
 
-def sweep_summary(device, step: int = 64, reps: int = 5) -> dict:
+def sweep_summary(device, step: int = 64, reps: int = 20) -> dict:
     """The tile/wave-quantization sweep at a coarse step for the benchmark line:
     fp16 M = 2304, K = 4096, N = 1536 .. 6144 every `step` columns, the
     planner's plan, inputs N(0,1)/sqrt(K) from a seeded device generator (B is
     the first N columns of one 4096 x 6144 draw, made contiguous).  Each point
-    is the median of `reps` event-timed calls after two warm-ups, with one
-    persistent workspace; reported as TFLOP/s over the points."""
+    is the mean of `reps` calls issued back to back between two events, after
+    untimed calls that keep the GPU busy (a quarter second before the first
+    point, 20 ms before each later one), with one persistent workspace;
+    reported as TFLOP/s over the points."""
     import torch
     import tiled_gemm_02_amd as tg
     from gemm_inputs import sweep_ns
@@ -510,20 +555,16 @@ def sweep_summary(device, step: int = 64, reps: int = 5) -> dict:
     stream = torch.cuda.current_stream(device)
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=device)
     pts = []
+    first = True
     for N in sweep_ns(step=step):
         B = Bfull[:, :N].contiguous()
         C = torch.empty((M, N), dtype=torch.float16, device=device)
-        for _ in range(2):
+
+        def call(_i=0):
             tg.gemm(A, B, out=C, workspace=ws, stream=stream.cuda_stream)
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            tg.gemm(A, B, out=C, workspace=ws, stream=stream.cuda_stream)
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ms = sorted(ts)[len(ts) // 2]
+        settle(call, device, SETTLE_S if first else 0.02)
+        first = False
+        ms = time_back_to_back(call, stream, reps)
         pl = tg.tg_gemm_plan(M, N, K, tg.TG_F16, tg.TG_NN)
         pts.append((N, 2.0 * M * N * K / ms / 1e9, pl))
     tf = sorted(v for _, v, _ in pts)
@@ -541,11 +582,12 @@ def sweep_summary(device, step: int = 64, reps: int = 5) -> dict:
                          "frac": round(mean / peak, 4), "traffic": None}}
 
 
-def sweep(out_path: str, step: int, reps: int = 5, tune: bool = False):
+def sweep(out_path: str, step: int, reps: int = 20, tune: bool = False):
     """fp16 M=2304, K=4096, N = 1536 .. 6144: the planner's tile against a fixed 256 x 256 one.
 
-    Inputs are N(0,1)/sqrt(K), seeded; each point is the median of `reps` timed calls after two
-    warm-up calls, from HIP events on the launch stream."""
+    Inputs are N(0,1)/sqrt(K), seeded; each point is the mean of `reps` calls issued back to
+    back between two HIP events on the launch stream, after untimed calls that keep the GPU
+    busy (a quarter second before the first point, 20 ms before each later one)."""
     import torch
     import tiled_gemm_02_amd as tg
     from gemm_inputs import F16, NN, sweep_ns
@@ -562,18 +604,14 @@ def sweep(out_path: str, step: int, reps: int = 5, tune: bool = False):
     # split-K partials go to one persistent workspace (as in the timed bench)
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=device)
 
+    first = [True]
+
     def timed(B, C, opts):
-        for _ in range(2):
+        def call(_i=0):
             tg.gemm(A, B, out=C, options=opts, workspace=ws, stream=stream.cuda_stream)
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            tg.gemm(A, B, out=C, options=opts, workspace=ws, stream=stream.cuda_stream)
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[len(ts) // 2]
+        settle(call, device, SETTLE_S if first[0] else 0.02)
+        first[0] = False
+        return time_back_to_back(call, stream, reps)
 
     rows = []
     tuned = []   # (N, planner TFLOP/s, best TFLOP/s, best options)
@@ -639,12 +677,13 @@ def sweep(out_path: str, step: int, reps: int = 5, tune: bool = False):
     print("\n".join(lines))
 
 
-def align_sweep(out_path: str, reps: int = 5):
+def align_sweep(out_path: str, reps: int = 20):
     """fp16 NN products of about 4096^3 with one size off the 16-byte grid: K = 4096 + d
     (rows of A off the grid) and M = N = 4096 + d (ragged tiles and rows of B and C off
     the grid) for d = 0 .. 16 (the alignment effect of "Matrix Multiplication Background
     User's Guide", section 2.2, Figure 2).  Aligned sizes take the LDS-DMA kernels directly, the
-    others aligned copies (staged in float32 when M or N is off the grid)."""
+    others aligned copies (staged in float32 when M or N is off the grid).  Each point is the
+    mean of `reps` calls issued back to back after untimed calls that keep the GPU busy."""
     import torch
     import tiled_gemm_02_amd as tg
     device = torch.device("cuda:0")
@@ -665,17 +704,11 @@ def align_sweep(out_path: str, reps: int = 5):
         B = (torch.randn((K, N), generator=g, device=device) / math.sqrt(K)).half()
         C = torch.empty((M, N), dtype=torch.float16, device=device)
         pl = tg.plan_for(A, B)
-        for _ in range(2):
+
+        def call(_i=0):
             tg.gemm(A, B, out=C, stream=stream.cuda_stream)
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            tg.gemm(A, B, out=C, stream=stream.cuda_stream)
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ms = sorted(ts)[len(ts) // 2]
+        settle(call, device, SETTLE_S if M == N == K == 4096 else 0.02)
+        ms = time_back_to_back(call, stream, reps)
         tf = 2.0 * M * N * K / ms / 1e9
         loads = {0: "element-wise", 1: "vector", 2: "copied", 3: "copied as NT"}[pl["vector_io"]]
         # plan_for assumes packed operands; the real call sees the same strides here
@@ -692,8 +725,9 @@ def stream_k_compare(out_path: str, reps: int = 20):
     (split_k = TG_SPLIT_STREAM_K) and forced 256 x 256 tiles without a split, on
     the M = 2304, K = 4096 quantization shapes that leave CUs idle, the bf16
     6912 x 2048 x 4096 shape, and small-M/N, large-K products.  Each point is the
-    median of `reps` event-timed calls after 3 warm-ups, with a 256 MiB caller
-    workspace; inputs N(0, 1)/64 from a seeded device generator."""
+    mean of `reps` calls issued back to back between two events, after untimed
+    calls that keep the GPU busy, with a 256 MiB caller workspace; inputs
+    N(0, 1)/64 from a seeded device generator."""
     import torch
     import tiled_gemm_02_amd as tg
     device = torch.device("cuda:0")
@@ -702,23 +736,19 @@ def stream_k_compare(out_path: str, reps: int = 20):
     ws = torch.empty(256 << 20, dtype=torch.uint8, device=device)
     tg.tune_cache_clear()
 
+    first = [True]
+
     def timed(A, B, C, opts):
-        for _ in range(3):
+        def call(_i=0):
             tg.gemm(A, B, out=C, options=opts, workspace=ws, stream=stream.cuda_stream)
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            tg.gemm(A, B, out=C, options=opts, workspace=ws, stream=stream.cuda_stream)
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[len(ts) // 2]
+        settle(call, device, SETTLE_S if first[0] else 0.05)
+        first[0] = False
+        return time_back_to_back(call, stream, reps)
 
     lines = ["# Stream-K against whole-tile plans (one MI355X)", "",
              "Command (repository root, one MI355X):", "", "```",
              f"python3 bench.py --stream-k-compare {out_path}", "```", "",
-             "Each point: median of event-timed calls after warm-up, 256 MiB caller workspace;",
+             "Each point: mean of calls issued back to back after untimed busy calls, 256 MiB caller workspace;",
              "TFLOP/s = 2MNK / time.", "",
              "| Shape | dtype | Planner's plan | Planner TFLOP/s | Stream-K TFLOP/s (us) | 256x256, no split |",
              "|---|---|---|---|---|---|"]
@@ -890,6 +920,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": SETTLE_S, "steps": r["settle_steps"]},
         "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -922,7 +953,7 @@ def main():
             p = rs["p"]
             sec.append({"workload": name, "value": ent["achieved"], "unit": "GB/s",
                         "ms_per_step": round(rs["ms_per_step"], 5),
-                        "steps": max(args.steps, 50), "warmup": args.warmup,
+                        "steps": max(args.steps, 50), "warmup": args.warmup, "settle_steps": rs["settle_steps"],
                         "config": {"M": p.M, "N": p.N, "dtype": rs["d"]["dtype"],
                                    "waves_per_row": rs["shape"][0], "chunks_per_lane": rs["shape"][1]},
                         "roofline": ent, "rotated_copies": rs["d"]["copies"]})
@@ -937,7 +968,7 @@ def main():
         sec.append({"workload": name, "value": ent["achieved"], "unit": ent["unit"],
                     "ms_per_step": round(rs["ms_per_step"], 5),
                     "us_per_step": round(rs["ms_per_step"] * 1e3, 2),
-                    "steps": max(args.steps, 50), "warmup": args.warmup,
+                    "steps": max(args.steps, 50), "warmup": args.warmup, "settle_steps": rs["settle_steps"],
                     "config": {"M": p.M, "N": p.N, "K": p.K, "dtype": rs["d"]["dtype"],
                                "layout": ["NN", "TN", "NT", "TT"][p.trans],
                                "epilogue": rs["d"]["epi"] or "none",
