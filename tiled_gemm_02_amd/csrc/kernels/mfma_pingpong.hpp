@@ -339,8 +339,63 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
                 mfma_drain();   // tied asm accumulators: the hazard the compiler cannot see
         }
 
-        // ---- epilogue: each lane holds runs of 4 consecutive columns of C
         T *C = (T *)p.C;
+        // ---- epilogue through LDS (16-bit C, written directly, no old C):
+        // the waves park their results in the ring as a row-major BM x 256
+        // tile, then every store instruction writes two whole rows of the
+        // tile, 16 bytes per lane.  The MFMA layout stores 16 rows x 32 bytes
+        // per instruction instead, four times the L2 requests for the same
+        // bytes, and all workgroups of a wave of tiles store at once.
+        if constexpr (!SK && MI == 16 && Tr::kBytes == 2 && BM * 512 <= S * STAGE) {
+            if (p.splits == 1 && p.oe.beta == 0.0f) {
+                // Every LDS read of the ring was consumed by an MFMA before the
+                // last barrier of the loop, and every copy had landed.  Chunk q
+                // (16 bytes) of row r sits at chunk q ^ (r & 15): the 8-byte
+                // writes below and the 16-byte reads after are bank-conflict-free.
+                char *ct = lds;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int r = wm * WM + 16 * i + (lane & 15);
+                        const int c = wn * WN + 16 * j + 4 * (lane >> 4);
+                        T o[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            o[e] = Tr::from_f32(out_value(p.oe, acc[i][j][e], 0.0f));
+                        u32x2 w;
+                        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
+                        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, o[2]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
+                        *(u32x2 *)(ct + r * 512 + (((c >> 3) ^ (r & 15)) << 4) + ((c >> 2) & 1) * 8) = w;
+                    }
+                __syncthreads();
+                const bool vec8 = (((uintptr_t)p.C) & 15) == 0 && (p.ldc & 7) == 0;
+                constexpr int RW = BM / 8;   // tile rows per wave
+#pragma unroll
+                for (int it = 0; it < RW / 2; ++it) {
+                    const int r = wave * RW + 2 * it + (lane >> 5), q = lane & 31;
+                    const u32x4 v = *(const u32x4 *)(ct + r * 512 + ((q ^ (r & 15)) << 4));
+                    const int m = m0 + r, n = n0 + 8 * q;
+                    if (m < p.M) {
+                        T *dst = C + (int64_t)m * p.ldc + n;
+                        if (vec8 && n + 7 < p.N) {
+                            *(u32x4 *)dst = v;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const uint32_t word = v[e >> 1];
+                                if (n + e < p.N)
+                                    dst[e] = __builtin_bit_cast(T, (uint16_t)(word >> (16 * (e & 1))));
+                            }
+                        }
+                    }
+                }
+                return;
+            }
+        }
+        // ---- epilogue: each lane holds runs of 4 consecutive columns of C
         float *W = p.ws + (int64_t)z * p.M * p.N;
         auto store4 = [&](int m, int n, const f32x4 &v) {
             if constexpr (SK) {
