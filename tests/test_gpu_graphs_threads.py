@@ -29,8 +29,12 @@ def test_graph_capture_replays_match_eager():
     dev = torch.device("cuda:0")
     # a whole-tile product, a split-K product (reduction kernel), a stream-K
     # product (fix-up kernel), 192 x 256 tiles, a float32 NN product through
-    # its transposing copy, and a row softmax, all with caller workspace
+    # its transposing copy, skinny and GEMV split-K products (reduction
+    # kernels) and a row softmax, all with one caller workspace
     probs = [(make_problem(1024, 1024, 1024, F16, NN, "normal", seed=71), None),
+             (make_problem(1024, 128, 4096, F16, NN, "normal", seed=77),
+              dict(path=tg.TG_PATH_SKINNY, split_k=4)),
+             (make_problem(1, 2048, 8192, F16, NN, "normal", seed=78), dict(path=tg.TG_PATH_GEMV, split_k=16)),
              (make_problem(256, 256, 8192, F16, NT, "normal", seed=72), dict(split_k=8)),
              (make_problem(1024, 1024, 4096, F16, NN, "normal", seed=73),
               dict(split_k=tg.TG_SPLIT_STREAM_K)),
@@ -58,9 +62,13 @@ def test_graph_capture_replays_match_eager():
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         work(s.cuda_stream)
+    A1, B1, o1, p1 = ins[1]
+    C1 = torch.empty_like(outs[1])
     for rep in range(3):
         for t in outs + [Y]:
             t.fill_(float("nan"))     # eager work between replays
+        # an eager call on the same workspace leaves its own partials there
+        tg.gemm(A1, B1, out=C1, options=o1, workspace=ws, stream=s.cuda_stream)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

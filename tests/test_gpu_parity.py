@@ -347,6 +347,37 @@ def test_split_partials_ignore_stale_workspace(case):
         assert r["ok"], (case, fill, r)
 
 
+@pytest.mark.parametrize("case", ["gemv", "gemv_generic", "skinny", "skinny_ragged"])
+def test_split_reduction_many_splits(case):
+    """Split-K products of the skinny and GEMV kernels at a few splits and at
+    more than 255 (a K range of one stage or a few rows per split): the fixed-
+    order reduction matches the oracle on a workspace of arbitrary bytes, and
+    a repeated call on the same workspace is bit-identical."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    if case == "gemv":            # 16-byte rows: the vector kernel
+        M, N, K, splits, opts = 1, 512, 8192, (16, 512), dict(path=tg.TG_PATH_GEMV)
+    elif case == "gemv_generic":  # odd n: the element-wise kernel
+        M, N, K, splits, opts = 1, 509, 4100, (12, 300), dict(path=tg.TG_PATH_GEMV)
+    elif case == "skinny":
+        M, N, K, splits, opts = 256, 128, 16448, (4, 257), dict(path=tg.TG_PATH_SKINNY)
+    else:                         # a ragged row block, columns past N in the tile
+        M, N, K, splits, opts = 200, 72, 16456, (3, 258), dict(path=tg.TG_PATH_SKINNY)
+    p = make_problem(M, N, K, F16, NN, "uniform", seed=13)
+    g = torch.Generator(device="cuda:0").manual_seed(6)
+    for s in splits:
+        o = dict(opts, split_k=s)
+        pl = tg.tg_gemm_plan(M, N, K, F16, NN, o)
+        _say("case split reduction", case, s, pl["split_k"], pl["workspace_bytes"])
+        assert pl["path"] == opts["path"] and pl["split_k"] > 1
+        assert (pl["split_k"] > 255) == (s > 255)
+        ws = torch.randint(0, 256, (pl["workspace_bytes"],), dtype=torch.uint8, device="cuda:0", generator=g)
+        r, got, _ = check_full(p, options=o, workspace=ws)
+        assert r["ok"], (case, s, r)
+        again = run_gpu(p, options=o, workspace=ws)
+        assert np.array_equal(got, again), (case, s)
+
+
 # ---------------------------------------------------------------- skinny path
 
 @pytest.mark.parametrize("dtype", [F16, BF16])
