@@ -226,16 +226,25 @@ def time_workload(name: str, steps: int, warmup: int, device, rotate: bool):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize(device)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # the timed steps run back to back between two events: an event after
+    # every step would add a queue marker to each microsecond-scale step
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize(device)
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    # per-step times (median, minimum) from a second, separately timed pass
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record(stream)
     for i in range(steps):
         step(i)
         evs[i + 1].record(stream)
     torch.cuda.synchronize(device)
-    wall = time.perf_counter() - t0
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    total_ms = evs[0].elapsed_time(evs[-1])
     plan = tg.plan_for(d["As"][0], d["Bs"][0], trans_a=p.trans_a, trans_b=p.trans_b)
     per_sorted = sorted(per)
     return dict(name=name, p=p, d=d, ms_per_step=total_ms / steps,
@@ -274,13 +283,13 @@ def time_softmax(name: str, steps: int, warmup: int, device):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize(device)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    evs[0].record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for i in range(steps):
         step(i)
-        evs[i + 1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize(device)
-    total_ms = evs[0].elapsed_time(evs[-1])
+    total_ms = e0.elapsed_time(e1)
     q, c = tg.softmax_shape(p.N, p.dtype)
     return dict(name=name, p=p, d=d, ms_per_step=total_ms / steps, shape=(q, c), settle_steps=n_settle)
 
@@ -500,9 +509,9 @@ def kernel_stats_summarize(root: str, out_path: str):
            "the bench's own HIP-event figure from the profiled run (kernel tracing serialises the",
            "launches, so profiled steps run somewhat longer than unprofiled ones); a step holds the",
            "dominant kernel and, where the plan splits K, the reduction, so the kernel average must",
-           "not exceed it.  Calls / Avg / Min / Max cover the launches of the timed region only (the",
-           "warm-up launches, the first of them cold, are left out); the table of all kernels below",
-           "counts every launch.", "",
+           "not exceed it.  Calls / Avg / Min / Max cover the launches after the warm-up: the timed",
+           "pass and the per-step pass that follows it (the settle and warm-up launches, the first",
+           "of them cold, are left out); the table of all kernels below counts every launch.", "",
            "| Bench line | Step (us) | Dominant kernel | Grid | Calls | Avg (us) | Min (us) | Max (us) | Avg <= step |",
            "|---|---|---|---|---|---|---|---|---|"]
     for ln in lines:
@@ -515,10 +524,11 @@ def kernel_stats_summarize(root: str, out_path: str):
             out.append(f"| {wl} | {step_us:.1f} | (no matching dispatch) | | | | | | |")
             continue
         (name, gx, gy), v = max(hit, key=lambda kv: len(kv[1]))
-        # the launches of the timed region: the last `steps` of the group (the
-        # warm-up launches come first, the coldest among them)
+        # the launches after the warm-up: the timed pass and the per-step pass,
+        # `steps` each, come last in the group (the settle and warm-up
+        # launches come first, the coldest among them)
         n_timed = ln.get("steps") or max(int(line.get("steps", 50)), 50)
-        v = v[-n_timed:]
+        v = v[-2 * n_timed:]
         avg = sum(v) / len(v)
         short = name.replace("void tg::", "").split("(")[0]
         out.append(f"| {wl} | {step_us:.1f} | `{short}` | {gx} x {gy} | {len(v)} | {avg:.1f} | {min(v):.1f} | "

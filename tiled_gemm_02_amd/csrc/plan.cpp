@@ -29,18 +29,22 @@ namespace tg {
 // with that tile's kernel, measured at 8192^3 fp16 on MI355X (256 x 256: the
 // ping-pong kernel, about 1250 TFLOP/s under the board's power limit; the
 // others: the 4-wave LDS-DMA kernel).
+// sat: fitted to MI355X timings with one to four workgroups per CU (fp16
+// 2304 x N x 4096 for N = 1536 .. 2560, 1024 x 1024 x 4096,
+// 512 x 512 x 16384, 256 x 256 x 65536; float32 256^3 and 512^3): the small
+// tiles need two or three workgroups per CU to hide their load latency.
 static const TileSpec kTiles16[] = {
-    {256, 256, 0.50, 160}, {192, 256, 0.42, 140}, {256, 128, 0.355, 96}, {128, 128, 0.385, 64},
-    {128, 64, 0.31, 48},   {64, 64, 0.22, 32},
+    {256, 256, 0.50, 160, 1.0}, {192, 256, 0.42, 140, 1.0}, {256, 128, 0.355, 96, 1.0},
+    {128, 128, 0.385, 64, 2.0}, {128, 64, 0.31, 48, 2.5},   {64, 64, 0.22, 32, 2.0},
 };
 // float32: 256 x 256 is the ping-pong kernel, K-contiguous A and B only
 // (tile_fits); the smaller tiles are the register-staged kernel.  Measured at
 // 8192^3 on MI355X: 137.6 TFLOP/s (NT, 256 x 256) and 126 (NN, 128 x 128) of
 // the 157.3 TFLOP/s float32 matrix peak.
 static const TileSpec kTiles32[] = {
-    {256, 256, 0.87, 160},
-    {128, 128, 0.80, 64},
-    {64, 64, 0.48, 32},
+    {256, 256, 0.87, 160, 1.0},
+    {128, 128, 0.80, 64, 2.0},
+    {64, 64, 0.48, 32, 2.0},
 };
 
 int tile_menu(int dtype, const TileSpec **out)
@@ -229,7 +233,8 @@ struct Cand {
     double t, eff;
 };
 
-static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int occ, double eff)
+static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int occ, double eff,
+                  double sat)
 {
     Cand c{};
     const int BK = 8 * chunk_elems(p.dtype);
@@ -245,7 +250,14 @@ static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int
     c.units = c.tiles * c.s;
     const int64_t slots = (int64_t)chip.num_cus * occ;
     c.waves = (c.units + slots - 1) / slots;
-    const double t_unit = occ * (2.0 * bm * bn * (double)kps) / (flop_rate_cu(chip, p.dtype) * eff);
+    // A CU holding c workgroups at once runs at eff * min(1, c / sat) of its
+    // peak (eff is measured with the tile's full residency, so sat <= occ),
+    // shared among the c: one workgroup takes max(c, sat) times its work at
+    // eff.  c is occ when the grid fills every slot, fewer when it is smaller.
+    const int64_t per_cu = (c.units + chip.num_cus - 1) / chip.num_cus;
+    const double conc = (double)std::min<int64_t>(occ, per_cu);
+    const double t_unit = std::max(conc, std::min(sat, (double)occ)) * (2.0 * bm * bn * (double)kps) /
+                          (flop_rate_cu(chip, p.dtype) * eff);
     // the tile kernel: waves of tiles, or its own HBM traffic (operands, and
     // the float32 partials it writes when K is split), whichever is longer
     const double partials = c.s > 1 ? (double)c.s * p.M * p.N * 4.0 : 0.0;
@@ -313,7 +325,7 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
     const bool vec = vec_ok(p);
     const int E = chunk_elems(p.dtype);
     const int BK = 8 * E;
-    const TileSpec generic = {64, 64, 0.42, 32};
+    const TileSpec generic = {64, 64, 0.42, 32, 2.0};
     const TileSpec *menu;
     int nmenu;
     if (vec) {
@@ -340,7 +352,7 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
                 return TG_ERR_UNSUPPORTED;
             }
             // the model prices any tile (e.g. another chip's tile menu)
-            forced = TileSpec{opts->tile_m, opts->tile_n, 1.0, 0};
+            forced = TileSpec{opts->tile_m, opts->tile_n, 1.0, 0, 1.0};
             f = &forced;
         }
         menu = f;
@@ -389,7 +401,7 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
                                           : model_occupancy(p.dtype, ts.bm, ts.bn, vec));
         occ = std::max(1, occ);
         for (int j = 0; j < nsplit; ++j) {
-            Cand c = price(p, chip, ts.bm, ts.bn, splits[j], occ, ts.eff);
+            Cand c = price(p, chip, ts.bm, ts.bn, splits[j], occ, ts.eff, ts.sat);
             if (!have) {
                 best = c;
                 have = true;

@@ -38,6 +38,8 @@ struct TileSpec {
     int bm, bn;
     double eff;      // fraction of the dense matrix peak a saturated CU sustains
     int lds_kib;     // LDS per workgroup (2 stages)
+    double sat;      // workgroups one CU needs at once to sustain eff (a lone small
+                     // tile cannot hide its own load latency)
 };
 
 int tile_menu(int dtype, const TileSpec **out);       // vector-load tiles, largest first
