@@ -84,11 +84,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _K = "tiled_gemm_02_amd/csrc/kernels/"
 # The sources each kernel family's code comes from: its counters are void once
 # any of them changes.
-KERNEL_SOURCES = {
-    "mfma": [_K + "common.hpp", _K + "mfma_gemm.hpp", _K + "mfma_gemm3.hpp", _K + "mfma_pingpong.hpp"],
-    "skinny": [_K + "common.hpp", _K + "skinny.hpp"],
-    "gemv": [_K + "common.hpp", _K + "gemv.hpp"],
-    "softmax": [_K + "common.hpp", _K + "softmax.hpp"],
+KERNEL_SOURCES = {   # instances.inc: the instantiations and launch shapes (e.g. the ring depth)
+    "mfma": [_K + "common.hpp", _K + "instances.inc", _K + "mfma_gemm.hpp", _K + "mfma_gemm3.hpp",
+             _K + "mfma_pingpong.hpp"],
+    "skinny": [_K + "common.hpp", _K + "instances.inc", _K + "skinny.hpp"],
+    "gemv": [_K + "common.hpp", _K + "instances.inc", _K + "gemv.hpp"],
+    "softmax": [_K + "common.hpp", _K + "instances.inc", _K + "softmax.hpp"],
 }
 
 
