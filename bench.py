@@ -510,9 +510,9 @@ def kernel_stats_summarize(root: str, out_path: str):
            "the bench's own HIP-event figure from the profiled run (kernel tracing serialises the",
            "launches, so profiled steps run somewhat longer than unprofiled ones); a step holds the",
            "dominant kernel and, where the plan splits K, the reduction, so the kernel average must",
-           "not exceed it.  Calls / Avg / Min / Max cover the launches after the warm-up: the timed",
-           "pass and the per-step pass that follows it (the settle and warm-up launches, the first",
-           "of them cold, are left out); the table of all kernels below counts every launch.", "",
+           "not exceed it.  Calls / Avg / Min / Max cover the launches of the timed pass only (the",
+           "settle and warm-up launches before it, the first of them cold, and the per-step pass",
+           "after it are left out); the table of all kernels below counts every launch.", "",
            "| Bench line | Step (us) | Dominant kernel | Grid | Calls | Avg (us) | Min (us) | Max (us) | Avg <= step |",
            "|---|---|---|---|---|---|---|---|---|"]
     for ln in lines:
@@ -525,11 +525,11 @@ def kernel_stats_summarize(root: str, out_path: str):
             out.append(f"| {wl} | {step_us:.1f} | (no matching dispatch) | | | | | | |")
             continue
         (name, gx, gy), v = max(hit, key=lambda kv: len(kv[1]))
-        # the launches after the warm-up: the timed pass and the per-step pass,
+        # the launches of the timed pass: the timed pass and the per-step pass,
         # `steps` each, come last in the group (the settle and warm-up
         # launches come first, the coldest among them)
         n_timed = ln.get("steps") or max(int(line.get("steps", 50)), 50)
-        v = v[-2 * n_timed:]
+        v = v[-2 * n_timed:-n_timed]
         avg = sum(v) / len(v)
         short = name.replace("void tg::", "").split("(")[0]
         out.append(f"| {wl} | {step_us:.1f} | `{short}` | {gx} x {gy} | {len(v)} | {avg:.1f} | {min(v):.1f} | "
