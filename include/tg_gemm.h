@@ -143,7 +143,9 @@ typedef struct tg_plan {
                             3 (float32) = the same copies laid out K-contiguous (A as M x K,
                             B as N x K, transposing operands stored the other way; when the
                             operands are aligned only those are copied) and the product
-                            run as TG_NT */
+                            run as TG_NT; 4 (16-bit, skinny) = B alone first copied into a
+                            zero-padded 16-byte-aligned buffer at the start of the workspace
+                            (its rows rounded up to 8 elements), A read in place */
     int64_t tiles;       /* ceil(M/tile_m) * ceil(N/tile_n) */
     int64_t workgroups;  /* tiles * split_k (MFMA/skinny), the stream-K workgroups, or the GEMV grid */
     int64_t waves;       /* ceil(workgroups / (num_cus * occupancy)) */

@@ -400,6 +400,43 @@ def test_skinny(dtype, trans, shape):
 
 @pytest.mark.parametrize("dtype", [F16, BF16])
 @pytest.mark.parametrize("trans", [NN, NT])
+@pytest.mark.parametrize("shape", [(300, 2, 1024), (1000, 3, 2048), (256, 5, 520), (640, 7, 4096),
+                                   (777, 12, 1032), (2000, 20, 1024), (400, 100, 512)])
+def test_skinny_narrow_outputs(dtype, trans, shape):
+    """Narrow products with N off the 16-byte grid (2 <= N <= 128, N % 8 != 0)
+    take the skinny kernel: stored N x K, B is read in place; stored K x N with
+    ldb = N, B alone is first copied into an aligned zero-padded buffer
+    (vector_io 4) and A is read in place.  Ragged M, a forced split, the
+    epilogue and alpha / beta through both forms."""
+    import tiled_gemm_02_amd as tg
+    M, N, K = shape
+    _say("case skinny narrow", dtype, trans, shape)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=14)
+    pl = tg.tg_gemm_plan(M, N, K, dtype, trans)
+    assert pl["path"] == tg.TG_PATH_SKINNY and pl["vector_io"] == (1 if trans == NT else 4), pl
+    r, _, _ = check_full(p)
+    assert r["ok"], r
+    r, _, _ = check_full(p, epilogue="leaky_relu", options=dict(path=tg.TG_PATH_SKINNY, split_k=3))
+    assert r["ok"], r
+    r, _, _ = check_scaled(p, 0.5, -1.0, epilogue="leaky_relu")
+    assert r["ok"], r
+
+
+def test_skinny_narrow_workload_size():
+    """8192 x 4 x 8192 (B K x N with ldb = 4, copied) and 8192 x 12 x 8192 NT,
+    the full matrix against the oracle."""
+    import tiled_gemm_02_amd as tg
+    for N, trans in ((4, NN), (12, NT)):
+        p = make_problem(8192, N, 8192, F16, trans, "normal", seed=15)
+        pl = tg.tg_gemm_plan(8192, N, 8192, F16, trans)
+        assert pl["path"] == tg.TG_PATH_SKINNY, pl
+        _say("case skinny narrow 8192", N, trans)
+        r, _, _ = check_full(p)
+        assert r["ok"], (N, trans, r)
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+@pytest.mark.parametrize("trans", [NN, NT])
 @pytest.mark.parametrize("shape", [(128, 128, 256), (200, 64, 264), (1000, 120, 1000), (136, 8, 512),
                                    (584, 72, 1096), (4160, 128, 2048)])
 def test_skinny_tall_row_blocks(dtype, trans, shape):

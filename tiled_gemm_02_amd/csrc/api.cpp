@@ -656,6 +656,29 @@ static int gemm_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda
             }
         }
     }
+    if (pl.vector_io == 4) {
+        // the skinny kernel on an aligned, zero-padded copy of B; A in place
+        const bool tb = trans & TG_TRANS_B;
+        const int64_t brows = tb ? N : K, bcols = tb ? K : N;
+        const int64_t bld = skinny_b_ld(p);
+        char *w = (char *)ws;
+        const hipError_t e = launch_pack(dtype, B, ldb, brows, bcols, w, brows, bld, s, false);
+        if (e != hipSuccess) {
+            if (own_ws)
+                (void)hipFreeAsync(ws, s);
+            return fail(TG_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+        }
+        tg_plan inner = pl;
+        inner.vector_io = 1;
+        Problem r = p;
+        r.ldb = bld;
+        rc = run_plan(inner, r, A, w, C, epi, w + skinny_b_bytes(p), s);
+        if (own_ws)
+            (void)hipFreeAsync(ws, s);
+        if (rc != TG_OK)
+            return rc;
+        return ok();
+    }
     if (pl.vector_io == 2 || pl.vector_io == 3) {
         // copy A and B into zero-padded aligned buffers (3: laid out for the NT
         // product, transposing where needed), then run the aligned plan

@@ -444,16 +444,32 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
 
 // ---------------------------------------------------------------- skinny
 
+// The skinny kernel reads A in place as K-contiguous rows of 16-byte chunks
+// (K and lda multiples of 8, A's pointer aligned) and B by 16-byte chunks of
+// its rows (ldb a multiple of 8, B's pointer aligned).  M and N may be ragged:
+// the buffer bounds read rows past M as zeros, the B copies skip chunks past
+// N, and the C stores are masked (any ldc).  Buffer offsets are 32-bit with
+// bit 31 reserved as "out of range": one row block of A, and all of B, must
+// span less than 2^31 bytes.
+static bool skinny_a_ok(const Problem &p)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    return p.dtype != TG_F32 && !(p.trans & TG_TRANS_A) && p.N >= 1 && p.N <= kSkinnyMaxN &&
+           p.M >= 2 * kSkinnyRows && p.K % 8 == 0 && p.lda % 8 == 0 && p.ptrs_aligned &&
+           (int64_t)kSkinnyMaxRows * p.lda * 2 < lim;
+}
+
 static bool skinny_fits(const Problem &p)
 {
-    // buffer offsets are 32-bit with bit 31 reserved as "out of range": one
-    // 64-row block of A, and all of B, must span less than 2^31 bytes
     const int64_t lim = (int64_t)1 << 31;
     const bool tb = (p.trans & TG_TRANS_B) != 0;
-    const bool fit32 = (int64_t)kSkinnyMaxRows * p.lda * 2 < lim && (tb ? p.N : p.K) * p.ldb * 2 < lim;
-    return p.dtype != TG_F32 && p.N <= kSkinnyMaxN && p.N >= 8 && p.M >= 2 * kSkinnyRows &&
-           vec_ok(p) && !(p.trans & TG_TRANS_A) && fit32;
+    return skinny_a_ok(p) && p.ldb % 8 == 0 && (tb ? p.N : p.K) * p.ldb * 2 < lim;
 }
+
+// B stored with rows off the 16-byte grid (ldb not a multiple of 8, e.g. a
+// K x N matrix with a few columns): the skinny kernel runs on an aligned,
+// zero-padded copy of B (skinny_b_ld).
+static bool skinny_b_copy(const Problem &p) { return skinny_a_ok(p) && p.N >= 2 && p.ldb % 8 != 0; }
 
 static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opts, tg_plan *out,
                        const char **why)
@@ -463,9 +479,9 @@ static int plan_skinny(const Problem &p, const Chip &chip, const tg_options *opt
         return TG_ERR_UNSUPPORTED;
     }
     if (!skinny_fits(p)) {
-        *why = "skinny path needs 16-bit operands, A not transposed, 8 <= N <= 128, M >= 128, "
-               "dimensions and leading dimensions multiples of 8, 16-byte aligned, and operand "
-               "spans below 2 GiB";
+        *why = "skinny path needs 16-bit operands, A not transposed, 1 <= N <= 128, M >= 128, "
+               "K, lda and ldb multiples of 8, A and B 16-byte aligned, and operand spans below "
+               "2 GiB";
         return TG_ERR_UNSUPPORTED;
     }
     const int BK = kSkinnyBK;
@@ -677,7 +693,31 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
             *out = direct;
         return rc_d;
     }
-    if (allow_pack && !vec_ok(p) && pack_worthwhile(p) && !(opts && opts->path == TG_PATH_GEMV)) {
+    const bool tile_forced = opts && (opts->tile_m > 0 || opts->tile_n > 0);
+    const bool skinny_ok = kSkinnyEnabled &&
+                           ((!opts || opts->path == TG_PATH_AUTO) ? !tile_forced : opts->path == TG_PATH_SKINNY);
+    const double ridge = chip_peak(chip, p.dtype) / (chip.hbm_gbs * 1e9);
+    const bool narrow = p.M > 1 && p.N > 1 && out->arith_intensity < ridge;
+    if (allow_pack && skinny_ok && narrow && skinny_b_copy(p)) {
+        // a narrow product whose B rows are off the 16-byte grid: copy B alone
+        // (K x N is small) and stream A in place with the skinny kernel
+        Problem q = p;
+        q.ldb = skinny_b_ld(p);
+        tg_plan inner;
+        const char *why_s = none;
+        if (plan_skinny(q, chip, opts, &inner, &why_s) == TG_OK) {
+            const uint64_t bbytes = skinny_b_bytes(p);
+            *out = inner;
+            out->vector_io = 4;
+            out->workspace_bytes = bbytes + inner.workspace_bytes;
+            out->pred_us += 2.0 * (double)bbytes / (chip.hbm_gbs * 1e3) + chip.launch_us;
+            fill_common(p, chip, out);
+            return TG_OK;
+        }
+    }
+    // (a narrow product the skinny kernel reads as it lies needs no copies)
+    if (allow_pack && !vec_ok(p) && pack_worthwhile(p) && !(opts && opts->path == TG_PATH_GEMV) &&
+        !(skinny_ok && narrow && skinny_fits(p))) {
         // plan the padded, aligned copy ("Matrix Multiplication Background
         // User's Guide", section 2.2, Table 1 and Figure 2: 16-bit products run
         // best with sizes that are multiples of 8 elements; padding is how a
@@ -708,7 +748,6 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
     if (path == TG_PATH_AUTO && opts && (opts->tile_m > 0 || opts->tile_n > 0))
         path = TG_PATH_MFMA;  // a forced macro tile means the macro-tile kernel
     if (path == TG_PATH_AUTO) {
-        const double ridge = chip_peak(chip, p.dtype) / (chip.hbm_gbs * 1e9);
         if (p.M == 1 || p.N == 1)
             path = TG_PATH_GEMV;
         else if (kSkinnyEnabled && skinny_fits(p) && out->arith_intensity < ridge)

@@ -99,6 +99,17 @@ Problem packed_problem(const Problem &p, bool nt = false);
 // kernels read in place: a tile's 256 rows then span less than 2^31 bytes.
 constexpr int64_t kDmaMaxLd16 = (int64_t)1 << 22;
 
+// The aligned copy of B behind a vector_io 4 plan (the skinny kernel with B's
+// rows off the 16-byte grid): B stored K x N is copied with rows of N rounded
+// up to 8 elements, B stored N x K with rows of K; zero-padded, at the start
+// of the workspace, 256-byte aligned size.
+inline int64_t skinny_b_ld(const Problem &p) { return (p.trans & TG_TRANS_B) ? p.K : (p.N + 7) / 8 * 8; }
+inline uint64_t skinny_b_bytes(const Problem &p)
+{
+    const int64_t rows = (p.trans & TG_TRANS_B) ? p.N : p.K;
+    return ((uint64_t)(rows * skinny_b_ld(p) * 2) + 255) & ~(uint64_t)255;
+}
+
 // 16-byte-chunk element count of a storage type.
 inline int chunk_elems(int dtype) { return dtype == TG_F32 ? 4 : 8; }
 inline int elem_bytes(int dtype) { return dtype == TG_F32 ? 4 : 2; }
