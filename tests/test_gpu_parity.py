@@ -750,29 +750,35 @@ def test_unaligned_operands_copied(case):
     assert r["ok"], (case, r)
 
 
-# M or N off the grid as well: the copies are padded in M and N too and the
-# macro-tile kernel stores only the M x N corner (ragged tails in every
-# dimension, padded C rows, scaled forms, a forced K split).
+# M or N off the grid as well (ragged tails in every dimension, padded C
+# rows, scaled forms).  Where the off-grid size is the one the 16-byte chunks
+# run along (M with A stored transposed, N with B stored plain), the copies
+# are padded in M and N too and the macro-tile kernel stores only the M x N
+# corner; a 16-bit M with A plain or N with B transposed is read in place (the
+# LDS-DMA kernels clamp rows past M and N); a narrow product copies B alone.
 PADDED_MN_CASES = [
-    # M, N, K, dtype, trans, ld_pad
-    (1025, 1000, 1031, F16, NN, 0),
-    (999, 1024, 1024, BF16, TN, 2),
-    (1024, 1003, 600, F16, NT, 0),
-    (517, 1021, 1000, BF16, TT, 1),
-    (1001, 1000, 999, F32, NN, 0),
-    (8191, 100, 1000, F16, NN, 0),
+    # M, N, K, dtype, trans, ld_pad, (path, vector_io)
+    (1025, 1000, 1031, F16, NN, 0, ("mfma", 2)),
+    (999, 1024, 1024, BF16, TN, 2, ("mfma", 2)),
+    (1024, 1003, 600, F16, NT, 0, ("mfma", 1)),
+    (517, 1021, 1000, BF16, TT, 1, ("mfma", 2)),
+    (1001, 1000, 999, F32, NN, 0, ("mfma", 3)),
+    (8191, 100, 1000, F16, NN, 0, ("skinny", 4)),
+    (1003, 1024, 1000, F16, NN, 0, ("mfma", 1)),
+    (1003, 1001, 1024, BF16, NT, 0, ("mfma", 1)),
+    (3, 4096, 4096, F16, NN, 0, ("mfma", 1)),
+    (12, 2048, 1024, BF16, NT, 0, ("mfma", 1)),
 ]
 
 
 @pytest.mark.parametrize("case", PADDED_MN_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}-p{c[5]}")
-def test_unaligned_rows_and_columns_copied(case):
+def test_unaligned_rows_and_columns(case):
     import tiled_gemm_02_amd as tg
-    M, N, K, dtype, trans, pad = case
-    _say("case padded copy", case)
+    M, N, K, dtype, trans, pad, (path, vio) = case
+    _say("case ragged M / N", case)
     p = make_problem(M, N, K, dtype, trans, "uniform", seed=53, ld_pad=pad)
     pl = tg.tg_plan_model(M, N, K, dtype, trans)
-    want = 3 if dtype == F32 and trans != NT else 2
-    assert pl["vector_io"] == want and pl["path_name"] == "mfma"
+    assert (pl["path_name"], pl["vector_io"]) == (path, vio), pl
     r, _, _ = check_full(p, out_pad=3)
     assert r["ok"], (case, r)
     r, _, _ = check_scaled(p, 0.5, -1.0, epilogue="leaky_relu", c_seed=7)

@@ -120,18 +120,24 @@ static void fill_common(const Problem &p, const Chip &chip, tg_plan *out)
     out->arith_intensity = bytes > 0 ? 2.0 * p.M * p.N * p.K / bytes : 0.0;
 }
 
-// Operands the 128-bit-load kernels take as they lie: sizes, leading
-// dimensions and base pointers on the 16-byte grid.  16-bit operands then run
-// on the LDS-DMA kernels, which address a tile's rows by 32-bit byte offsets
-// from a per-tile base: leading dimensions up to kDmaMaxLd16 elements.  Wider
-// rows are read through aligned copies (or element-wise loads).
+// Operands the 128-bit-load kernels take as they lie: leading dimensions,
+// base pointers and the dimensions the 16-byte chunks run along on the
+// 16-byte grid.  16-bit operands run on the LDS-DMA kernels, whose chunks run
+// along each operand's contiguous dimension (K for A plain and B transposed,
+// M for A transposed, N for B plain) and which clamp the rows past M and N, so
+// M (A plain) and N (B transposed) may be ragged; they address a tile's rows
+// by 32-bit byte offsets from a per-tile base: leading dimensions up to
+// kDmaMaxLd16 elements.  Float32 keeps every dimension on the grid.  Other
+// operands are read through aligned copies (or element-wise loads).
 static bool vec_ok(const Problem &p)
 {
     const int E = chunk_elems(p.dtype);
     if (p.dtype != TG_F32 && (p.lda > kDmaMaxLd16 || p.ldb > kDmaMaxLd16))
         return false;
-    return p.ptrs_aligned && p.M % E == 0 && p.N % E == 0 && p.K % E == 0 && p.lda % E == 0 &&
-           p.ldb % E == 0;
+    const bool ta = (p.trans & TG_TRANS_A) != 0, tb = (p.trans & TG_TRANS_B) != 0;
+    const bool m_ok = p.M % E == 0 || (p.dtype != TG_F32 && !ta);
+    const bool n_ok = p.N % E == 0 || (p.dtype != TG_F32 && tb);
+    return p.ptrs_aligned && m_ok && n_ok && p.K % E == 0 && p.lda % E == 0 && p.ldb % E == 0;
 }
 
 // ---------------------------------------------------------------- GEMV
