@@ -785,6 +785,34 @@ def test_unaligned_rows_and_columns(case):
     assert r["ok"], (case, r)
 
 
+# One operand off the grid beside a large aligned one: only the small operand
+# is copied (the workspace holds a few columns or rows, not the large
+# operand), the large one is read in place.
+ONE_COPY_CASES = [
+    # M, N, K, dtype, trans: A stored transposed and aligned, B K x 7 copied
+    (2048, 7, 4096, F16, TN),
+    # A stored K x 7 copied, B stored N x K read in place
+    (7, 2048, 4096, BF16, TT),
+    # A plain with M ragged read in place, B K x 5 copied
+    (3001, 5, 2048, F16, NN),
+]
+
+
+@pytest.mark.parametrize("case", ONE_COPY_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}")
+def test_only_the_off_grid_operand_is_copied(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, dtype, trans = case
+    _say("case one copy", case)
+    p = make_problem(M, N, K, dtype, trans, "uniform", seed=55)
+    pl = tg.tg_plan_model(M, N, K, dtype, trans)
+    assert pl["vector_io"] in (2, 4), pl
+    assert pl["workspace_bytes"] < 2 * max(M, N) * K // 8, pl
+    r, _, _ = check_full(p)
+    assert r["ok"], (case, r)
+    r, _, _ = check_scaled(p, 0.5, -1.0, epilogue="leaky_relu", c_seed=9)
+    assert r["ok"], (case, r)
+
+
 def test_padded_copy_with_forced_split():
     p = make_problem(1025, 1000, 4100, F16, NN, "uniform", seed=54)
     for split in (1, 3):

@@ -567,6 +567,22 @@ void softmax_shape(int dtype, int64_t N, int *q, int *c)
 
 static int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Which operands the (non-transposing) aligned copies must copy.  A K tail
+// off the 16-byte grid pads K in both (the padding must be zeros in both).
+// Otherwise a 16-bit operand is copied only when the LDS-DMA kernels cannot
+// read it as it lies (vec_ok's rules for that operand); float32 copies both.
+static void copy_needs(const Problem &p, bool *a, bool *b)
+{
+    const int E = chunk_elems(p.dtype);
+    const bool ta = (p.trans & TG_TRANS_A) != 0, tb = (p.trans & TG_TRANS_B) != 0;
+    if (p.dtype == TG_F32 || p.K % E != 0 || !p.ptrs_aligned) {
+        *a = *b = true;
+        return;
+    }
+    *a = p.lda % E != 0 || (ta && p.M % E != 0) || p.lda > kDmaMaxLd16;
+    *b = p.ldb % E != 0 || (!tb && p.N % E != 0) || p.ldb > kDmaMaxLd16;
+}
+
 Problem packed_problem(const Problem &p, bool nt)
 {
     const int E = chunk_elems(p.dtype);
@@ -580,17 +596,27 @@ Problem packed_problem(const Problem &p, bool nt)
             q.ldb = p.K;
         return q;
     }
-    q.M = round_up(p.M, E);
-    q.N = round_up(p.N, E);
-    q.K = round_up(p.K, E);
     if (nt) {
+        q.M = round_up(p.M, E);
+        q.N = round_up(p.N, E);
+        q.K = round_up(p.K, E);
         q.trans = TG_NT;
         q.lda = q.K;
         q.ldb = q.K;
-    } else {
-        q.lda = (p.trans & TG_TRANS_A) ? q.M : q.K;
-        q.ldb = (p.trans & TG_TRANS_B) ? q.K : q.N;
+        q.ptrs_aligned = true;
+        return q;
     }
+    // an operand read in place keeps its sizes and leading dimension, so no
+    // kernel reads it past its own M or N
+    bool a, b;
+    copy_needs(p, &a, &b);
+    q.K = round_up(p.K, E);
+    q.M = a ? round_up(p.M, E) : p.M;
+    q.N = b ? round_up(p.N, E) : p.N;
+    if (a)
+        q.lda = (p.trans & TG_TRANS_A) ? q.M : q.K;
+    if (b)
+        q.ldb = (p.trans & TG_TRANS_B) ? q.K : q.N;
     q.ptrs_aligned = true;
     return q;
 }
@@ -612,7 +638,7 @@ PackLayout pack_layout(const Problem &p, bool nt)
         L.b_rows = q.N;
         L.b_cols = q.K;
     } else {
-        L.a_copy = L.b_copy = true;
+        copy_needs(p, &L.a_copy, &L.b_copy);
         L.a_trans = L.b_trans = false;
         L.a_rows = ta ? q.K : q.M;
         L.a_cols = ta ? q.M : q.K;
@@ -627,15 +653,23 @@ PackLayout pack_layout(const Problem &p, bool nt)
 }
 
 // Worth copying: the element-wise kernel runs at a few percent of the vector
-// ones, so above about 1 GFLOP (20 us of element-wise work) the copies (two
-// short launches and one pass over A and B) pay for themselves many times.
-// The transposing copy moves 64 x 64 blocks through LDS; it is priced at this
-// fraction of the HBM rate.
+// ones, so above about 1 GFLOP (20 us of element-wise work) the copies (short
+// launches and one pass over what they copy) pay for themselves many times.
+// For 16-bit operands they also pay above 4 MB of operands: the element-wise
+// kernel streams about 0.5 TB/s, a tenth of a copy pass, and the copies take
+// only the operands the LDS-DMA kernels cannot read in place.  Float32
+// copies are laid out for the NT kernel, transposing whole operands, which
+// measured slower than the element-wise kernel on narrow products below
+// 1 GFLOP (8192 x 7 x 8192: 205 against 160 us).  Below both, the launches
+// would cost more than they save.  The transposing copy moves 64 x 64 blocks
+// through LDS; it is priced at this fraction of the HBM rate.
 static constexpr double kTransposeHbmFrac = 0.6;
 
 static bool pack_worthwhile(const Problem &p)
 {
-    return p.M > 1 && p.N > 1 && 2.0 * (double)p.M * (double)p.N * (double)p.K >= 1e9;
+    return p.M > 1 && p.N > 1 &&
+           (2.0 * (double)p.M * (double)p.N * (double)p.K >= 1e9 ||
+            (p.dtype != TG_F32 && alg_bytes(p) >= 4e6));
 }
 
 int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_options *opts,
