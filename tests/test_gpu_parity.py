@@ -505,6 +505,29 @@ def test_gemv_strip_widths_and_splits(dtype, lanes, split):
     assert r["ok"], r
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_gemv_ragged_lengths_on_aligned_rows(dtype):
+    """Output lengths and K off the 16-byte grid with row strides on it (padded
+    views): the vector cols kernel reads the chunk that straddles column n
+    element by element (every strip width, with and without splits), the
+    vector rows kernel reads the K tail element by element."""
+    import tiled_gemm_02_amd as tg
+    E = 4 if dtype == F32 else 8
+    # M, N, K, trans, ld_pad (puts the padded leading dimensions on the grid), options
+    cases = [(1, 4097, 1000, NN, 7, None), (1, 1001, 2048, NN, 7, None), (301, 1, 777, TT, 3, None),
+             (1, 523, 1037, NN, 5, dict(path=tg.TG_PATH_GEMV, tile_n=8 * E, split_k=3)),
+             (1, 523, 1037, NN, 5, dict(path=tg.TG_PATH_GEMV, tile_n=64 * E, split_k=1)),
+             (1, 700, 1003, NT, 5, None), (500, 1, 1029, NT, 3, None)]
+    for M, N, K, trans, pad, opts in cases:
+        _say("case gemv ragged", dtype, M, N, K, trans, pad, opts)
+        p = make_problem(M, N, K, dtype, trans, "uniform", seed=16, ld_pad=pad)
+        assert p.lda % 8 == 0 or M == 1, p.lda
+        r, _, _ = check_full(p, options=opts)
+        assert r["ok"], (M, N, K, trans, r)
+        r, _, _ = check_scaled(p, 0.5, -1.0, epilogue="leaky_relu", options=opts, c_seed=10)
+        assert r["ok"], (M, N, K, trans, r)
+
+
 def test_gemv_strided():
     p = make_problem(1, 600, 256, F16, NN, "uniform", seed=10, ld_pad=8)
     r, _, _ = check_full(p, out_pad=0)

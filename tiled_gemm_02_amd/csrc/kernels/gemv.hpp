@@ -96,8 +96,10 @@ __global__ __launch_bounds__(256) void gemv_cols_kernel(GemvArgs p)
     for (int e = 0; e < E; ++e)
         acc[e] = 0.f;
 
-    // n is a multiple of E on this path, so a chunk is wholly in or out
-    if (col < p.n) {
+    // the chunk holding column n - 1 may end past n (n need not be a multiple
+    // of E, and the matrix may end at column n of its last row): that lane
+    // loads it element by element
+    if (col + E <= p.n) {
         int k = k_lo + slot;
         for (; k + (U - 1) * SLOTS < k_hi; k += U * SLOTS) {
             u32x4 x[U];
@@ -124,6 +126,14 @@ __global__ __launch_bounds__(256) void gemv_cols_kernel(GemvArgs p)
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 acc[e] += a * f[e];
+        }
+    } else if (col < p.n) {
+        for (int k = k_lo + slot; k < k_hi; k += SLOTS) {
+            const float a = load_scalar<Tr>(p.V, (int64_t)k * p.vs);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                if (col + e < p.n)
+                    acc[e] += a * Tr::to_f32(base[(int64_t)k * p.ldx + e]);
         }
     }
 
@@ -152,11 +162,13 @@ __global__ __launch_bounds__(256) void gemv_cols_kernel(GemvArgs p)
         float *W = p.ws + (int64_t)blockIdx.y * p.n + col;
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            W[e] = s[e];
+            if (col + e < p.n)
+                W[e] = s[e];
     } else {
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            gemv_store<Tr>(p, col + e, s[e]);
+            if (col + e < p.n)
+                gemv_store<Tr>(p, col + e, s[e]);
     }
 }
 

@@ -168,10 +168,12 @@ static int plan_gemv(const Problem &p, const Chip &chip, const tg_options *opts,
         // vector loads need a unit-stride, aligned vector and aligned rows
         const int64_t vs = (p.M == 1) ? (ta ? p.lda : 1) : (tb ? 1 : p.ldb);
         const int64_t ldx = (p.M == 1) ? p.ldb : p.lda;
-        out->vector_io = p.ptrs_aligned && vs == 1 && ldx % E == 0 && p.K % E == 0;
+        // (the kernel reads a K tail past the last whole chunk element by element)
+        out->vector_io = p.ptrs_aligned && vs == 1 && ldx % E == 0;
     } else {
         const int64_t ldx = (p.M == 1) ? p.ldb : p.lda;
-        const bool vec = p.ptrs_aligned && n % E == 0 && ldx % E == 0;
+        // (the chunk that straddles column n is read element by element)
+        const bool vec = p.ptrs_aligned && ldx % E == 0;
         int64_t cols_per_wg = 64LL * E;  // element-wise kernel: 64 lanes x E columns
         int64_t rows_per_pass = 4;       // rows its workgroup covers per load
         if (vec) {
