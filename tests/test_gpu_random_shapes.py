@@ -1,10 +1,11 @@
 """Seeded random products against the float64 oracle (run with -m gpu).
 
-A fixed list of cases drawn from one seed: sizes from 1 to 700 in every
+Fixed lists of cases drawn from two seeds: sizes from 1 to 700 in every
 dimension (aligned and not, so the vector, padded-copy and element-wise loads
 all occur), every storage type and layout, padded leading dimensions, the
 LeakyReLU epilogue, alpha / beta, and forced K splits or tiles where the
-operands allow them.  Every output element is compared with the oracle.
+operands allow them; and 16-bit narrow, few-row and ragged products.  Every
+output element is compared with the oracle.
 """
 from __future__ import annotations
 
@@ -64,6 +65,38 @@ def _cases(n=200, seed=2024):
 
 
 CASES = _cases()
+
+
+def _cases_narrow_and_ragged(n=80, seed=2025):
+    """16-bit products the planner reads in place or copies one operand of:
+    narrow outputs (N from 2 to 130, the skinny kernel, B copied alone when its
+    rows are off the grid), a few rows (M from 2 to 16) beside a large B, and
+    ragged M and N with K on the grid (the LDS-DMA kernels clamping rows), in
+    every layout."""
+    rng = np.random.default_rng(seed)
+
+    def pick(xs):
+        return xs[int(rng.integers(0, len(xs)))]
+
+    out = []
+    for i in range(n):
+        kind = rng.random()
+        dtype = pick([F16, BF16])
+        trans = pick([NN, NT, TN, TT])
+        K = int(rng.integers(1, 257)) * 8
+        if kind < 0.4:
+            M, N = int(rng.integers(128, 3001)), int(rng.integers(2, 131))
+        elif kind < 0.7:
+            M, N = int(rng.integers(2, 17)), int(rng.integers(128, 3001))
+        else:
+            M, N = int(rng.integers(100, 1101)), int(rng.integers(100, 1101))
+        epi = "leaky_relu" if rng.random() < 0.3 else None
+        scaled = rng.random() < 0.3
+        out.append((200 + i, M, N, K, dtype, trans, 0, epi, scaled, None))
+    return out
+
+
+CASES += _cases_narrow_and_ragged()
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-d{c[4]}-t{c[5]}")
