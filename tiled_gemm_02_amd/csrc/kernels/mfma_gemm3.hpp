@@ -479,6 +479,62 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
         return;
     }
     T *C = (T *)p.C;
+    // 16-bit C without old C: through LDS as a row-major BM x BN tile, then
+    // whole rows, 16 bytes per lane (the MFMA layout stores 16 rows x 32 bytes
+    // per instruction).  Chunk q of row r sits at q ^ sw(r): XOR of the row's
+    // low four bits for rows of 16 or 32 chunks, of bits 1..3 for rows of 8
+    // (two such rows share one pass over the 64 banks), so the 8-byte writes
+    // and the 16-byte reads are both free of bank conflicts.
+    if constexpr (Tr::kBytes == 2 && BM * BN * 2 <= S * STAGE) {
+        if (p.oe.beta == 0.0f) {
+            constexpr int CH = BN / 8;                       // 16-byte chunks per row
+            auto sw = [](int r) { return CH >= 16 ? (r & 15) : ((r >> 1) & 7); };
+            char *ct = lds;
+            __syncthreads();   // every wave's last fragment reads are done
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int r = wm * WM + i * 16 + fr;
+                    const int c = wn * WN + j * 16 + 4 * fg;
+                    T o[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = Tr::from_f32(out_value(p.oe, acc[i][j][e], 0.0f));
+                    u32x2 w;
+                    w[0] = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
+                    w[1] = (uint32_t)__builtin_bit_cast(uint16_t, o[2]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
+                    *(u32x2 *)(ct + r * (BN * 2) + (((c >> 3) ^ sw(r)) << 4) + ((c >> 2) & 1) * 8) = w;
+                }
+            __syncthreads();
+            const bool vec8 = (((uintptr_t)p.C) & 15) == 0 && (p.ldc & 7) == 0;
+            constexpr int NWAVE = WGM * WGN;
+            constexpr int RPI = 64 / CH;                     // rows per read instruction
+            constexpr int RW = BM / NWAVE;                   // tile rows per wave
+#pragma unroll
+            for (int it = 0; it < RW / RPI; ++it) {
+                const int r = wave * RW + it * RPI + lane / CH, q = lane % CH;
+                const u32x4 v = *(const u32x4 *)(ct + r * (BN * 2) + ((q ^ sw(r)) << 4));
+                const int m = m0 + r, n = n0 + 8 * q;
+                if (m < p.M && n < p.N) {
+                    T *dst = C + (int64_t)m * p.ldc + n;
+                    if (vec8 && n + 7 < p.N) {
+                        *(u32x4 *)dst = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t word = v[e >> 1];
+                            if (n + e < p.N)
+                                dst[e] = __builtin_bit_cast(T, (uint16_t)(word >> (16 * (e & 1))));
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * WM + i * 16 + fr;
