@@ -455,6 +455,50 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
     }
 
     // ---- epilogue: lane holds C[m][n .. n+3] of every 16 x 16 block
+    if constexpr (BM * BN * 4 <= S * STAGE) {
+        if (p.splits > 1) {
+            // this split's float32 partial through LDS, like the 16-bit C below:
+            // a row-major BM x BN tile (chunk q of row r at q ^ (r & 15), rows of
+            // 16 or 32 chunks), then rows of 16-byte chunks per lane
+            constexpr int CH = BN / 4;
+            static_assert(CH >= 16, "float32 staging: rows of 16 or more chunks");
+            char *ct = lds;
+            __syncthreads();   // every wave's last fragment reads are done
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int r = wm * WM + i * 16 + fr;
+                    const int q = (wn * WN + j * 16) / 4 + fg;
+                    *(f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4)) = acc[i][j];
+                }
+            __syncthreads();
+            float *W = p.ws + (int64_t)z * p.M * p.N;
+            const bool wvec = (p.N & 3) == 0;
+            constexpr int RPI = 64 / CH;                     // rows per read instruction
+            constexpr int RW = BM / NW;                      // tile rows per wave
+#pragma unroll
+            for (int it = 0; it < RW / RPI; ++it) {
+                const int r = wave * RW + it * RPI + lane / CH, q = lane % CH;
+                const f32x4 v = *(const f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4));
+                const int m = m0 + r, n = n0 + 4 * q;
+                if (m < p.M && n < p.N) {
+                    float *dst = W + (int64_t)m * p.N + n;
+                    if (wvec && n + 3 < p.N) {
+                        *(f32x4 *)dst = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = v[e];
+                            if (n + e < p.N)
+                                dst[e] = x;
+                        }
+                    }
+                }
+            }
+            return;
+        }
+    }
     if (p.splits > 1) {
         float *W = p.ws + (int64_t)z * p.M * p.N;
 #pragma unroll
