@@ -395,6 +395,54 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
                 return;
             }
         }
+        // ---- K split: this split's float32 partial through LDS, one group's
+        // half of the tile (the whole ring) at a time: row-major rows of 16-byte
+        // chunks, chunk q of row r at q ^ (r & 15), then every wave stores rows
+        // of the half, 16 bytes per lane
+        if constexpr (!SK && MI == 16 && (BM / 2) * BN * 4 <= S * STAGE) {
+            if (p.splits > 1) {
+                constexpr int CH = BN / 4;      // 16-byte chunks per row
+                constexpr int RW = WM / 8;      // rows of a half per wave
+                char *ct = lds;
+                float *Wz = p.ws + (int64_t)z * p.M * p.N;
+                const bool wvec = (p.N & 3) == 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    __syncthreads();   // the ring is idle (or the last half is stored)
+                    if (grp == h) {
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < FN; ++j) {
+                                const int r = 16 * i + (lane & 15);
+                                const int q = (wn * WN + 16 * j) / 4 + (lane >> 4);
+                                *(f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4)) = acc[i][j];
+                            }
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int it = 0; it < RW * CH / 64; ++it) {
+                        const int r = wave * RW + (it * 64 + lane) / CH, q = (it * 64 + lane) % CH;
+                        const f32x4 v = *(const f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4));
+                        const int m = m0 + h * WM + r, n = n0 + 4 * q;
+                        if (m < p.M && n < p.N) {
+                            float *dst = Wz + (int64_t)m * p.N + n;
+                            if (wvec && n + 3 < p.N) {
+                                *(f32x4 *)dst = v;
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const float x = v[e];
+                                    if (n + e < p.N)
+                                        dst[e] = x;
+                                }
+                            }
+                        }
+                    }
+                }
+                return;
+            }
+        }
         // ---- epilogue: each lane holds runs of 4 consecutive columns of C
         float *W = p.ws + (int64_t)z * p.M * p.N;
         auto store4 = [&](int m, int n, const f32x4 &v) {
