@@ -547,6 +547,12 @@ def kernel_stats_summarize(root: str, out_path: str):
 
 # ---------------------------------------------------------------- quantization sweep
 
+def tile_label(pl: dict) -> str:
+    """Macro tile of a plan, marked when two K groups share each workgroup."""
+    t = f"{pl['tile_m']}x{pl['tile_n']}"
+    return t + " x2K" if pl.get("k_groups", 1) == 2 else t
+
+
 def sweep_summary(device, step: int = 64, reps: int = 20) -> dict:
     """The tile/wave-quantization sweep at a coarse step for the benchmark line:
     fp16 M = 2304, K = 4096, N = 1536 .. 6144 every `step` columns, the
@@ -587,7 +593,7 @@ def sweep_summary(device, step: int = 64, reps: int = 20) -> dict:
             "value": round(mean, 2), "mean": round(mean, 2), "median": round(tf[len(tf) // 2], 2),
             "min": round(tf[0], 2), "max": round(tf[-1], 2),
             "median_n_le_1792": round(low[len(low) // 2], 2) if low else None,
-            "per_point": [[n, round(v, 1), f"{pl['tile_m']}x{pl['tile_n']}", pl["split_k"], pl["tiles"]]
+            "per_point": [[n, round(v, 1), tile_label(pl), pl["split_k"], pl["tiles"]]
                           for n, v, pl in pts],
             "roofline": {"bound": "mfma", "achieved": round(mean, 2), "peak": peak, "unit": "TFLOP/s",
                          "frac": round(mean / peak, 4), "traffic": None}}
@@ -633,15 +639,15 @@ def sweep(out_path: str, step: int, reps: int = 20, tune: bool = False):
         ms = timed(B, C, None)
         ms_f = timed(B, C, fixed)
         fl = 2.0 * M * N * K
-        rows.append((N, pl["tile_m"], pl["tile_n"], pl["split_k"], pl["tiles"], pl["waves"],
+        rows.append((N, tile_label(pl), "", pl["split_k"], pl["tiles"], pl["waves"],
                      fl / ms / 1e9, fl / ms_f / 1e9, pl["pred_eff"]))
-        msg = (f"N={N} plan {pl['tile_m']}x{pl['tile_n']} tiles {pl['tiles']} waves {pl['waves']}: "
+        msg = (f"N={N} plan {tile_label(pl)} tiles {pl['tiles']} waves {pl['waves']}: "
                f"{rows[-1][6]:.0f} TFLOP/s (fixed 256x256: {rows[-1][7]:.0f})")
         if tune:
             best, _ = tg.autotune(A, B, out=C, workspace=ws, reps=3)
             ms_b = timed(B, C, None if best["path"] == tg.TG_PATH_AUTO else best)
             tuned.append((N, fl / ms / 1e9, fl / ms_b / 1e9, best))
-            msg += f" (autotuned {best['tile_m']}x{best['tile_n']} s{best['split_k']}: {fl / ms_b / 1e9:.0f})"
+            msg += f" (autotuned {tile_label(best)} s{best['split_k']}: {fl / ms_b / 1e9:.0f})"
         log(msg)
     better = sum(1 for r in rows if r[6] >= r[7] * 0.98)
     mean_p = sum(r[6] for r in rows) / len(rows)
@@ -652,7 +658,8 @@ def sweep(out_path: str, step: int, reps: int = 20, tune: bool = False):
              f"{len(rows)} points, step {step}.  Mean TFLOP/s: planner {mean_p:.0f}, fixed 256x256 "
              f"{mean_f:.0f}; the planner is within 2 % of or above the fixed tile at {better} of "
              f"{len(rows)} points.", "",
-             "Bands of equal plan (tile, waves of 256 CUs); TFLOP/s min / median / max within the band:", "",
+             "Bands of equal plan (tile, waves of 256 CUs; x2K: two K groups per workgroup, summed in LDS); "
+             "TFLOP/s min / median / max within the band:", "",
              "| N range | Tile | Split | Tiles | Waves | Planner TFLOP/s | Fixed 256x256 TFLOP/s |",
              "|---|---|---|---|---|---|---|"]
     i = 0
@@ -664,7 +671,7 @@ def sweep(out_path: str, step: int, reps: int = 20, tune: bool = False):
         def mmm(k):
             v = sorted(r[k] for r in band)
             return f"{v[0]:.0f} / {v[len(v) // 2]:.0f} / {v[-1]:.0f}"
-        lines.append(f"| {band[0][0]}-{band[-1][0]} | {band[0][1]}x{band[0][2]} | {band[0][3]} | "
+        lines.append(f"| {band[0][0]}-{band[-1][0]} | {band[0][1]} | {band[0][3]} | "
                      f"{band[0][4]}-{band[-1][4]} | {band[0][5]} | {mmm(6)} | {mmm(7)} |")
         i = j + 1
     lines.append("")
@@ -680,7 +687,7 @@ def sweep(out_path: str, step: int, reps: int = 20, tune: bool = False):
         for (N, tp, tb, b) in tuned:
             if tp / tb < 0.95:
                 plan = "planner's" if b["path"] == tg.TG_PATH_AUTO else (
-                    f"{b['tile_m']}x{b['tile_n']} split {b['split_k']}" if b["path"] == tg.TG_PATH_MFMA
+                    f"{tile_label(b)} split {b['split_k']}" if b["path"] == tg.TG_PATH_MFMA
                     else f"skinny split {b['split_k']}")
                 lines.append(f"| {N} | {tp:.0f} | {tb:.0f} | {plan} |")
         lines += ["", "(rows listed: points where the planner is more than 5 % below the best)", ""]
@@ -723,7 +730,7 @@ def align_sweep(out_path: str, reps: int = 20):
         tf = 2.0 * M * N * K / ms / 1e9
         loads = {0: "element-wise", 1: "vector", 2: "copied", 3: "copied as NT"}[pl["vector_io"]]
         # plan_for assumes packed operands; the real call sees the same strides here
-        lines.append(f"| {M} | {N} | {K} | {pl['path_name']} | {pl['tile_m']}x{pl['tile_n']} | "
+        lines.append(f"| {M} | {N} | {K} | {pl['path_name']} | {tile_label(pl)} | "
                      f"{pl['split_k']} | {loads} | {ms * 1e3:.0f} | {tf:.0f} |")
         log(lines[-1])
     lines.append("")
@@ -776,7 +783,7 @@ def stream_k_compare(out_path: str, reps: int = 20):
         t_sk = timed(A, B, C, dict(split_k=tg.TG_SPLIT_STREAM_K))
         t_dp = timed(A, B, C, dict(tile_m=256, tile_n=256, split_k=1))
         name = "bf16" if dt == torch.bfloat16 else "fp16"
-        lines.append(f"| {M}x{N}x{K} | {name} | {pl['tile_m']}x{pl['tile_n']} split {pl['split_k']} | "
+        lines.append(f"| {M}x{N}x{K} | {name} | {tile_label(pl)} split {pl['split_k']} | "
                      f"{fl / t_p / 1e9:.0f} | {fl / t_sk / 1e9:.0f} ({t_sk * 1e3:.1f}) | {fl / t_dp / 1e9:.0f} |")
         log(lines[-1])
         del A, B, C
@@ -942,7 +949,7 @@ def main():
                    "layout": ["NN", "TN", "NT", "TT"][p.trans], "epilogue": d["epi"] or "none",
                    "alpha": d["alpha"], "beta": d["beta"],
                    "seed": p.desc["seed"], "dist": p.desc["dist"], "plan": {
-                       k: r["plan"][k] for k in ("path_name", "tile_m", "tile_n", "split_k",
+                       k: r["plan"][k] for k in ("path_name", "tile_m", "tile_n", "split_k", "k_groups",
                                                   "tiles", "waves", "occupancy")}},
         "bench_args": " ".join(sys.argv[1:]),
         "ms_median": round(r["ms_median"], 5),
@@ -985,7 +992,7 @@ def main():
                                "epilogue": rs["d"]["epi"] or "none",
                                "ai_flop_per_byte": round(rs["plan"]["arith_intensity"], 1)},
                     "plan": {k: rs["plan"][k] for k in ("path_name", "tile_m", "tile_n", "split_k",
-                                                         "tiles", "workgroups", "waves")},
+                                                         "k_groups", "tiles", "workgroups", "waves")},
                     "roofline": ent, "rotated_copies": rs["d"]["copies"]})
         del rs
         torch.cuda.empty_cache()

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define TG_VERSION 106
+#define TG_VERSION 107
 
 /* storage type of A, B and C */
 enum tg_dtype { TG_F32 = 0, TG_F16 = 1, TG_BF16 = 2 };
@@ -128,6 +128,11 @@ typedef struct tg_options {
     int32_t tile_n;  /* 0 = planner's choice, else a macro-tile width */
     int32_t split_k; /* 0 = planner's choice, 1 = no split, s > 1 = split K s ways,
                         TG_SPLIT_STREAM_K = stream-K */
+    int32_t k_groups; /* macro-tile path: 0 = planner's choice (1 when the tile is
+                         forced), 1 = one group of waves per workgroup, 2 = two groups
+                         of waves per workgroup, each taking half of the workgroup's K
+                         range, summed in LDS (16-bit 128 x 128 tiles); other values
+                         are TG_ERR_ARG, 2 where no such kernel exists TG_ERR_UNSUPPORTED */
 } tg_options;
 
 /* What the planner decided, and the quantization figures behind it. */
@@ -156,6 +161,10 @@ typedef struct tg_plan {
     double arith_intensity; /* 2MNK / (bytes of A, B and C), FLOP per byte */
     uint64_t workspace_bytes; /* float32 split-K partials or stream-K pieces, and aligned
                                  copies, the plan needs */
+    int32_t k_groups;    /* macro-tile path: groups of waves per workgroup splitting its K
+                            range, their sums added in LDS (no workspace, no second
+                            launch; "Matrix Multiplication Background User's Guide",
+                            section 2.3: splitting K); 1 elsewhere */
 } tg_plan;
 
 /* C = epi(alpha A . B + beta C) on the current HIP device.  epilogue may be

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert tg.tg_version() == 106
+    assert tg.tg_version() == 107
 
 
 def test_epilogue_struct_matches_header(tmp_path):
@@ -130,13 +130,14 @@ def _kernel_stubs():
 def test_every_planned_16bit_tile_has_kernels(dtype):
     """Every macro tile the planner may pick for 16-bit operands has its kernel
     compiled for all four layouts (256 x 256 and 192 x 256: the ping-pong
-    kernel; the others: the four-wave LDS-DMA kernel), so no plan can reach a
-    launcher without an instance."""
+    kernel; the others: the four-wave LDS-DMA kernel, 128 x 128 also with two
+    K groups), so no plan can reach a launcher without an instance."""
     import re
     stubs = _kernel_stubs()
-    for bm, bn in [(256, 128), (128, 128), (128, 64), (64, 64)]:
-        found = set(re.findall(rf"tg::mfma_gemm3_kernel<tg::{dtype}, {bm}, {bn}, \d+, 2, 2, (\w+), (\w+)>", stubs))
-        assert len(found) == 4, (bm, bn, found)
+    for bm, bn, kg in [(256, 128, 1), (128, 128, 1), (128, 64, 1), (64, 64, 1), (128, 128, 2)]:
+        found = set(re.findall(
+            rf"tg::mfma_gemm3_kernel<tg::{dtype}, {bm}, {bn}, \d+, 2, 2, (\w+), (\w+), {kg}>", stubs))
+        assert len(found) == 4, (bm, bn, kg, found)
     for bm in (256, 192):
         found = set(re.findall(rf"tg::mfma_pingpong_kernel<tg::{dtype}, \d, 16, (\w+), (\w+), false, {bm}>", stubs))
         assert len(found) == (4 if bm == 256 else 2), (bm, found)

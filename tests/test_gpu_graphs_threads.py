@@ -12,7 +12,7 @@ import threading
 import numpy as np
 import pytest
 
-from gemm_inputs import F16, F32, NN, NT, make_problem, make_softmax_input
+from gemm_inputs import BF16, F16, F32, NN, NT, make_problem, make_softmax_input
 from tests.gpu_helpers import to_device
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +28,8 @@ def test_graph_capture_replays_match_eager():
     _say("case graph capture")
     dev = torch.device("cuda:0")
     # a whole-tile product, a split-K product (reduction kernel), a stream-K
-    # product (fix-up kernel), 192 x 256 tiles, a float32 NN product through
+    # product (fix-up kernel), 192 x 256 tiles, 128 x 128 tiles with two K
+    # groups (alone, and with a K split), a float32 NN product through
     # its transposing copy, skinny and GEMV split-K products (reduction
     # kernels) and a row softmax, all with one caller workspace
     probs = [(make_problem(1024, 1024, 1024, F16, NN, "normal", seed=71), None),
@@ -39,6 +40,8 @@ def test_graph_capture_replays_match_eager():
              (make_problem(1024, 1024, 4096, F16, NN, "normal", seed=73),
               dict(split_k=tg.TG_SPLIT_STREAM_K)),
              (make_problem(768, 1024, 1024, F16, NN, "normal", seed=75), dict(tile_m=192, tile_n=256)),
+             (make_problem(2304, 1536, 1024, F16, NN, "normal", seed=79), dict(k_groups=2)),
+             (make_problem(520, 392, 4104, BF16, NT, "normal", seed=80), dict(k_groups=2, split_k=3)),
              (make_problem(1024, 1024, 1024, F32, NN, "normal", seed=76), dict(tile_m=256, tile_n=256))]
     assert tg.tg_gemm_plan(1024, 1024, 1024, tg.TG_F32, tg.TG_NN,
                            options=dict(tile_m=256, tile_n=256))["vector_io"] == 3

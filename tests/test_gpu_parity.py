@@ -203,6 +203,80 @@ def test_tile_192x256_is_planned_and_sampled():
     assert r["ok"], r
 
 
+# 16-bit 128 x 128 tiles with two K groups per workgroup (eight waves, each
+# group over its part of the workgroup's K range, group 1's sums added to group
+# 0's in LDS): every layout, ragged M (A plain) and N (B transposed), K tails in
+# either group, a group 1 one whole stage short (K = 136: 72 and 64, so group 1
+# runs an all-zero tail stage; K = 8: group 1 has no K at all), outer K splits
+# (the last split's halves uneven), alpha / beta (old C: the direct stores) and
+# the epilogue on the LDS-staged stores
+KG2_CASES = [
+    (296, 280, 136, F16, NN, 1, None, 1.0, 0.0),
+    (300, 264, 200, BF16, NT, 1, None, 1.0, 0.0),
+    (264, 300, 1032, F16, NT, 1, None, 1.0, 0.0),
+    (392, 520, 72, BF16, TN, 1, None, 1.0, 0.0),
+    (256, 256, 8, F16, TT, 1, None, 1.0, 0.0),
+    (520, 392, 4104, F16, NN, 3, None, 1.0, 0.0),
+    (136, 1000, 2056, BF16, TT, 2, None, 1.0, 0.0),
+    (296, 280, 264, F16, NT, 1, "leaky_relu", 1.0, 0.0),
+    (384, 512, 512, BF16, NN, 1, "leaky_relu", 0.5, -1.0),
+    (200, 136, 1000, F16, TN, 1, None, -1.25, 0.75),
+    (384, 512, 520, BF16, NT, 2, "leaky_relu", 0.5, -1.0),
+]
+
+
+@pytest.mark.parametrize("case", KG2_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}-s{c[5]}")
+def test_two_k_groups(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, dtype, trans, split, epi, alpha, beta = case
+    _say("case two K groups", case)
+    p = make_problem(M, N, K, dtype, trans, "normal", seed=41)
+    opts = dict(tile_m=128, tile_n=128, split_k=split, k_groups=2)
+    pl = tg.tg_gemm_plan(M, N, K, dtype, trans, options=opts)
+    assert pl["k_groups"] == 2 and pl["split_k"] == split, pl
+    if alpha == 1.0 and beta == 0.0:
+        r, _, _ = check_full(p, epilogue=epi, options=opts)
+    else:
+        r, _, _ = check_scaled(p, alpha, beta, epilogue=epi, options=opts)
+    assert r["ok"], (case, r)
+
+
+def test_two_k_groups_refused_where_no_kernel_exists():
+    """float32, tiles other than 128 x 128, the GEMV and skinny paths and
+    operands off the 16-byte grid have no two-group kernel: the call fails;
+    k_groups = 3 is an argument error."""
+    import tiled_gemm_02_amd as tg
+    for dtype, shape, opts in [(F32, (256, 256, 256), dict(k_groups=2)),
+                               (F16, (256, 256, 256), dict(tile_m=256, tile_n=256, k_groups=2)),
+                               (F16, (1, 256, 256), dict(path=tg.TG_PATH_GEMV, k_groups=2)),
+                               (F16, (300, 282, 130), dict(k_groups=2))]:
+        _say("case two K groups refused", dtype, shape, opts)
+        p = make_problem(*shape, dtype, NN, "normal", seed=42)
+        with pytest.raises(tg.TgError):
+            run_gpu(p, options=opts)
+    p = make_problem(256, 256, 256, F16, NN, "normal", seed=42)
+    with pytest.raises(tg.TgError):
+        run_gpu(p, options=dict(k_groups=3))
+
+
+def test_two_k_groups_planned_and_sampled():
+    """2304 x 1536 x 4096 (216 tiles of 128 x 128 for 256 CUs): the planner
+    puts each tile on one eight-wave workgroup whose two K groups share the K
+    loop, with no workspace; 4096 sampled outputs against the oracle, and the
+    same product with the planner's former choice (K split two ways through
+    float32 partials) agrees to the tolerance."""
+    import tiled_gemm_02_amd as tg
+    pl = tg.tg_gemm_plan(2304, 1536, 4096, tg.TG_F16, tg.TG_NN)
+    assert (pl["tile_m"], pl["tile_n"], pl["k_groups"], pl["split_k"]) == (128, 128, 2, 1), pl
+    assert pl["workspace_bytes"] == 0, pl
+    p = make_problem(2304, 1536, 4096, F16, NN, "normal", seed=0)
+    _say("case two K groups sampled")
+    r = check_sampled(p)
+    assert r["ok"], r
+    r = check_sampled(p, options=dict(tile_m=128, tile_n=128, split_k=2, k_groups=1))
+    assert r["ok"], r
+
+
 # float32 on the 256 x 256 ping-pong kernel: ragged M and N edges, a K tail
 # (K % 16 != 0: the partial stage goes through registers), K splits, the
 # epilogue and alpha / beta

@@ -4,7 +4,7 @@ Fixed lists of cases drawn from two seeds: sizes from 1 to 700 in every
 dimension (aligned and not, so the vector, padded-copy and element-wise loads
 all occur), every storage type and layout, padded leading dimensions, the
 LeakyReLU epilogue, alpha / beta, and forced K splits or tiles where the
-operands allow them; and 16-bit narrow, few-row and ragged products.  Every
+operands allow them; and 16-bit narrow, few-row and ragged products; and 128 x 128 tiles with two K groups.  Every
 output element is compared with the oracle.
 """
 from __future__ import annotations
@@ -97,6 +97,34 @@ def _cases_narrow_and_ragged(n=80, seed=2025):
 
 
 CASES += _cases_narrow_and_ragged()
+
+
+def _cases_two_k_groups(n=40, seed=2026):
+    """16-bit 128 x 128 tiles with two K groups per workgroup: every layout,
+    M and N from 8 to 700 (ragged where the layout reads them in place), K
+    from 8 to 3000 on the 16-byte grid (either group's tail, or group 1 one
+    whole stage short), outer K splits 1 to 3."""
+    rng = np.random.default_rng(seed)
+
+    def pick(xs):
+        return xs[int(rng.integers(0, len(xs)))]
+
+    out = []
+    for i in range(n):
+        dtype = pick([F16, BF16])
+        trans = pick([NN, NT, TN, TT])
+        M = int(rng.integers(8, 701)) if not (trans & 1) else int(rng.integers(1, 88)) * 8
+        N = int(rng.integers(8, 701)) if (trans & 2) else int(rng.integers(1, 88)) * 8
+        K = int(rng.integers(1, 376)) * 8
+        split = int(rng.integers(1, 4)) if K >= 384 else 1
+        epi = "leaky_relu" if rng.random() < 0.3 else None
+        scaled = rng.random() < 0.3
+        out.append((300 + i, M, N, K, dtype, trans, 0, epi, scaled,
+                    dict(tile_m=128, tile_n=128, split_k=split, k_groups=2)))
+    return out
+
+
+CASES += _cases_two_k_groups()
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-d{c[4]}-t{c[5]}")

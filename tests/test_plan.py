@@ -154,6 +154,41 @@ def test_unaligned_operands_are_copied_when_it_pays():
 
 
 
+def test_two_k_group_plans():
+    """128 x 128 tiles with two K groups per workgroup (eight waves splitting
+    the workgroup's K range, summed in LDS): one workgroup per CU, so the plan
+    uses them where the tiles about fill the CUs once and K is long enough to
+    share; a K split of two without partials, workspace or a second launch."""
+    F = tg.TG_F16
+    for n in (1536, 1664, 1792):     # 216-252 tiles on 256 CUs
+        p = tg.tg_plan_model(2304, n, 4096, F)
+        assert (p["tile_m"], p["tile_n"], p["k_groups"], p["split_k"]) == (128, 128, 2, 1), p
+        assert p["occupancy"] == 1 and p["waves"] == 1 and p["workspace_bytes"] == 0
+        # one group: the same tile needs a split of two (float32 partials) to fill the CUs
+        q = tg.tg_plan_model(2304, n, 4096, F, options=dict(k_groups=1))
+        assert q["k_groups"] == 1 and q["pred_us"] > p["pred_us"]
+    # 270 tiles would need two waves: not used there, nor for large products
+    assert tg.tg_plan_model(2304, 1920, 4096, F)["k_groups"] == 1
+    assert tg.tg_plan_model(8192, 8192, 8192, F)["k_groups"] == 1
+    # a forced tile keeps one group unless two are asked for
+    f = tg.tg_plan_model(2304, 1536, 4096, F, options=dict(tile_m=128, tile_n=128, split_k=2))
+    assert f["k_groups"] == 1 and f["workspace_bytes"] == 2 * 2304 * 1536 * 4
+    f = tg.tg_plan_model(2304, 1536, 4096, F, options=dict(tile_m=128, tile_n=128, split_k=2, k_groups=2))
+    assert f["k_groups"] == 2 and f["split_k"] == 2 and f["workgroups"] == 2 * 216
+    # other paths report one group
+    assert tg.tg_plan_model(1, 8192, 8192, F)["k_groups"] == 1
+    assert tg.tg_plan_model(8192, 128, 8192, F)["k_groups"] == 1
+    # no two-group kernel: float32, other tiles, other paths, off-grid operands; bad values
+    for args, opts in [((1024, 1024, 4096, tg.TG_F32), dict(k_groups=2)),
+                       ((1024, 1024, 4096, F), dict(k_groups=2, split_k=tg.TG_SPLIT_STREAM_K)),
+                       ((1, 1024, 4096, F), dict(k_groups=2, path=tg.TG_PATH_GEMV)),
+                       ((300, 282, 130, F), dict(k_groups=2)),
+                       ((1024, 1024, 4096, F), dict(k_groups=3)),
+                       ((1024, 1024, 4096, F), dict(k_groups=-1))]:
+        with pytest.raises(tg.TgError):
+            tg.tg_plan_model(*args, tg.TG_NN, options=opts)
+
+
 def test_stream_k_plans():
     """Stream-K (split_k = TG_SPLIT_STREAM_K): one workgroup per CU over all
     tiles' 32-deep K stages, 256 x 256 tiles, two float32 tile pieces of

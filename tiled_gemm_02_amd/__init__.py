@@ -44,7 +44,7 @@ class Epilogue(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-                ("split_k", ctypes.c_int32)]
+                ("split_k", ctypes.c_int32), ("k_groups", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -55,7 +55,8 @@ class Plan(ctypes.Structure):
                 ("workgroups", ctypes.c_int64), ("waves", ctypes.c_int64),
                 ("tile_eff", ctypes.c_double), ("wave_eff", ctypes.c_double),
                 ("pred_eff", ctypes.c_double), ("pred_us", ctypes.c_double),
-                ("arith_intensity", ctypes.c_double), ("workspace_bytes", ctypes.c_uint64)]
+                ("arith_intensity", ctypes.c_double), ("workspace_bytes", ctypes.c_uint64),
+                ("k_groups", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         d = {name: getattr(self, name) for name, _ in self._fields_}
@@ -157,7 +158,7 @@ def _opts(options) -> ctypes.POINTER(Options) | None:
         return None
     if isinstance(options, Options):
         return ctypes.pointer(options)
-    o = Options(TG_PATH_AUTO, 0, 0, 0)
+    o = Options(TG_PATH_AUTO, 0, 0, 0, 0)
     for k, v in dict(options).items():
         if k == "path" and isinstance(v, str):
             v = {n: c for c, n in PATH_NAMES.items()}[v]
@@ -392,13 +393,14 @@ def autotune(A, B, *, trans_a: bool = False, trans_b: bool = False, epilogue=Non
     ws_ptr, ws_bytes = (None, 0)
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    best = Options(TG_PATH_AUTO, 0, 0, 0)
+    best = Options(TG_PATH_AUTO, 0, 0, 0, 0)
     us = ctypes.c_float(0.0)
     _check(load().tg_autotune(M, N, K, A.data_ptr() if A.numel() else None, _ld(A),
                               B.data_ptr() if B.numel() else None, _ld(B), out.data_ptr(), _ld(out),
                               dtype, trans, _epi(epilogue), ws_ptr, ws_bytes, stream, int(reps),
                               ctypes.byref(best), ctypes.byref(us)))
-    opts = dict(path=best.path, tile_m=best.tile_m, tile_n=best.tile_n, split_k=best.split_k)
+    opts = dict(path=best.path, tile_m=best.tile_m, tile_n=best.tile_n, split_k=best.split_k,
+                k_groups=best.k_groups)
     return opts, float(us.value)
 
 

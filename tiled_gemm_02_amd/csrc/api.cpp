@@ -40,22 +40,22 @@ hipError_t launch_mfma2_sk(int dtype, int trans, const MfmaArgs &a, hipStream_t 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s)
+hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, int kg, const MfmaArgs &a, hipStream_t s)
 {
     switch (dtype) {
-    case TG_F16: return launch_mfma2_f16(trans, bm, bn, a, s);
-    case TG_BF16: return launch_mfma2_bf16(trans, bm, bn, a, s);
-    case TG_F32: return launch_mfma2_f32(trans, bm, bn, a, s);
+    case TG_F16: return launch_mfma2_f16(trans, bm, bn, kg, a, s);
+    case TG_BF16: return launch_mfma2_bf16(trans, bm, bn, kg, a, s);
+    case TG_F32: return launch_mfma2_f32(trans, bm, bn, kg, a, s);
     }
     return hipErrorInvalidValue;
 }
 
-int mfma2_occupancy(int dtype, int trans, int bm, int bn)
+int mfma2_occupancy(int dtype, int trans, int bm, int bn, int kg)
 {
     switch (dtype) {
-    case TG_F16: return mfma2_occupancy_f16(trans, bm, bn);
-    case TG_BF16: return mfma2_occupancy_bf16(trans, bm, bn);
-    case TG_F32: return mfma2_occupancy_f32(trans, bm, bn);
+    case TG_F16: return mfma2_occupancy_f16(trans, bm, bn, kg);
+    case TG_BF16: return mfma2_occupancy_bf16(trans, bm, bn, kg);
+    case TG_F32: return mfma2_occupancy_f32(trans, bm, bn, kg);
     }
     return 0;
 }
@@ -215,7 +215,7 @@ struct DeviceInfo {
     // taken once with this device current; null until then
     void *scratch_ptr = nullptr;
     // measured residency per (dtype, trans, tile, vec), 0 = not yet asked
-    int occ[3][4][8][2] = {};
+    int occ[3][4][8][2][2] = {};   // dtype, trans, tile, vector loads, K groups - 1
     // benchmark-mode winners (tg_autotune) per problem, used by calls that
     // pass no options; guarded by g_tune_mu
     std::map<TuneKey, tg_options> tuned;
@@ -313,20 +313,21 @@ static int tile_slot(int bm, int bn)
     return -1;
 }
 
-static int device_occ(int dtype, int trans, int bm, int bn, bool vec, void *ctx)
+static int device_occ(int dtype, int trans, int bm, int bn, bool vec, int kg, void *ctx)
 {
     DeviceInfo *d = (DeviceInfo *)ctx;
     const int ts = tile_slot(bm, bn);
-    if (ts < 0)
-        return model_occupancy(dtype, bm, bn, vec);
+    if (ts < 0 || kg < 1 || kg > 2)
+        return model_occupancy(dtype, bm, bn, vec, kg);
     std::lock_guard<std::mutex> lk(g_dev_mu);
-    int &slot = d->occ[dtype][trans][ts][vec ? 1 : 0];
+    int &slot = d->occ[dtype][trans][ts][vec ? 1 : 0][kg - 1];
     if (slot == 0) {
-        int n = use_mfma2(dtype, trans, vec, bm, bn, 0, 0) ? mfma2_occupancy(dtype, trans, bm, bn)
-                                                           : mfma_occupancy(dtype, trans, bm, bn, vec);
+        int n = use_mfma2(dtype, trans, vec, bm, bn, 0, 0) ? mfma2_occupancy(dtype, trans, bm, bn, kg)
+                : kg == 1                                   ? mfma_occupancy(dtype, trans, bm, bn, vec)
+                                                            : 0;
         slot = n > 0 ? n : -1;
     }
-    return slot > 0 ? slot : model_occupancy(dtype, bm, bn, vec);
+    return slot > 0 ? slot : model_occupancy(dtype, bm, bn, vec, kg);
 }
 
 // ---------------------------------------------------------------- validation
@@ -464,8 +465,11 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.splits = pl.split_k;
         if (pl.vector_io != 0 && p.dtype != TG_F32 && (p.lda > kDmaMaxLd16 || p.ldb > kDmaMaxLd16))
             return fail(TG_ERR_UNSUPPORTED, "16-bit vector-load plan with a leading dimension above 2^22");
-        if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, pl.tile_m, pl.tile_n, p.lda, p.ldb))
-            e = launch_mfma2(p.dtype, p.trans, pl.tile_m, pl.tile_n, a, s);
+        const bool dma = use_mfma2(p.dtype, p.trans, pl.vector_io != 0, pl.tile_m, pl.tile_n, p.lda, p.ldb);
+        if (pl.k_groups != 1 && !dma)
+            return fail(TG_ERR_UNSUPPORTED, "a plan with %d K groups needs the LDS-DMA kernels", pl.k_groups);
+        if (dma)
+            e = launch_mfma2(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.k_groups, a, s);
         else
             e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);
         if (e == hipSuccess && pl.split_k > 1)
@@ -857,7 +861,7 @@ int tg_autotune(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, con
     const int splits[] = {1, 2, 3, 4, 6, 8};
     for (int i = 0; i < nmenu; ++i)
         for (int sp : splits)
-            cands.push_back(tg_options{TG_PATH_MFMA, menu[i].bm, menu[i].bn, sp});
+            cands.push_back(tg_options{TG_PATH_MFMA, menu[i].bm, menu[i].bn, sp, menu[i].kg});
     cands.push_back(tg_options{TG_PATH_MFMA, 64, 64, 1});   // the element-wise tile
     cands.push_back(tg_options{TG_PATH_MFMA, 256, 256, TG_SPLIT_STREAM_K});
     for (int rb : {64, 128})

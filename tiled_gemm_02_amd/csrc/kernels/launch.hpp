@@ -17,9 +17,10 @@ hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, const Mfm
                        hipStream_t s);
 // Resident workgroups per CU of an instance (0 if none).
 int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec);
-// The LDS-DMA kernel for 16-bit, 16-byte-aligned operands (same tiles).
-hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s);
-int mfma2_occupancy(int dtype, int trans, int bm, int bn);
+// The LDS-DMA kernel for 16-bit, 16-byte-aligned operands (same tiles); kg = K
+// groups per workgroup (1, or 2 for the tiles built with two).
+hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, int kg, const MfmaArgs &a, hipStream_t s);
+int mfma2_occupancy(int dtype, int trans, int bm, int bn, int kg);
 // Stream-K with 256 x 256 tiles on a.splits workgroups (16-bit, aligned), then
 // the fix-up of the split tiles; a.ws holds 2 * a.splits float32 tiles.
 hipError_t launch_mfma2_sk(int dtype, int trans, const MfmaArgs &a, hipStream_t s);
@@ -60,8 +61,9 @@ hipError_t launch_softmax(int dtype, int q, int c, bool vec, const SoftmaxArgs &
     hipError_t launch_gemv_##NAME(bool rows_form, bool vec, int lpr, const GemvArgs &a,          \
                                   hipStream_t s);                                                \
     hipError_t launch_skinny_##NAME(bool trans_b, const SkinnyArgs &a, hipStream_t s);           \
-    hipError_t launch_mfma2_##NAME(int trans, int bm, int bn, const MfmaArgs &a, hipStream_t s); \
-    int mfma2_occupancy_##NAME(int trans, int bm, int bn);                                       \
+    hipError_t launch_mfma2_##NAME(int trans, int bm, int bn, int kg, const MfmaArgs &a,         \
+                                   hipStream_t s);                                               \
+    int mfma2_occupancy_##NAME(int trans, int bm, int bn, int kg);                               \
     hipError_t launch_mfma2_sk_##NAME(int trans, const MfmaArgs &a, hipStream_t s);              \
     hipError_t launch_softmax_##NAME(int q, int c, bool vec, const SoftmaxArgs &a, hipStream_t s);
 

@@ -266,14 +266,26 @@ __device__ __forceinline__ u32x4 frag3_mn(uint32_t b0, uint32_t b1, int n0)
     return out;
 }
 
-template <typename Tr, int BM, int BN, int S, int WGM, int WGN, bool TA, bool TB>
-__global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
+// KG K groups per workgroup (1 or 2): with 2, the workgroup holds two sets of
+// WGM x WGN waves, each running the pipeline above over its own part of the
+// workgroup's K range in its own LDS ring; at the end the second group's sums
+// are added to the first's through LDS (group 0 + group 1, a fixed order) and
+// the whole workgroup stores the tile.  It is a K split of two whose
+// reduction stays on the CU: no float32 partials in memory and no second
+// launch.  The groups meet at the same barriers, so both run the same number
+// of stages: group 0 takes the first ceil(klen / 16) * 8 elements of K (on the
+// 16-byte grid), group 1 the rest, and a group one whole stage short processes
+// an all-zero tail stage first.
+template <typename Tr, int BM, int BN, int S, int WGM, int WGN, bool TA, bool TB, int KG = 1>
+__global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArgs p)
 {
     // The LDS-DMA and transposed-read builtins exist on the device side only;
     // the host pass needs nothing but the signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = typename Tr::T;
-    constexpr int NW = WGM * WGN;                         // waves per workgroup
+    static_assert(KG == 1 || KG == 2, "one or two K groups");
+    constexpr int NW = WGM * WGN;                         // waves per K group
+    constexpr int NWALL = NW * KG;                        // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;           // wave sub-tile
     constexpr int FM = WM / 16, FN = WN / 16;
     using OpA = Dma3<BM, TA, NW>;
@@ -285,24 +297,34 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
     static_assert(FM >= 2 && FN >= 2, "wave sub-tile of at least 32 x 32");
     static_assert(S >= 2 && (S - 2) * NDMA < 64, "stage count");
 
-    __shared__ __attribute__((aligned(1024))) char lds[S * STAGE];
+    constexpr int LDS_BYTES = KG * S * STAGE;
+    __shared__ __attribute__((aligned(1024))) char lds_all[LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kgrp = wave_all / NW;                       // K group of this wave
+    const int wave = wave_all % NW;                       // wave within its group
     const int wm = wave / WGN, wn = wave % WGN;
+    char *const lds = lds_all + kgrp * (S * STAGE);       // this group's ring
 
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int z = blockIdx.y;
-    const int kbeg = z * p.kps;
-    const int klen = max(0, min(p.K, kbeg + p.kps) - kbeg);
+    const int kbeg_wg = z * p.kps;
+    const int klen_wg = max(0, min(p.K, kbeg_wg + p.kps) - kbeg_wg);
+    const int klen0 = KG == 1 ? klen_wg : 8 * ((klen_wg + 15) / 16);   // group 0's share
+    const int kbeg = kbeg_wg + (kgrp ? klen0 : 0);
+    const int klen = kgrp ? klen_wg - klen0 : klen0;
     // A partial last 64-deep stage (K not a multiple of 64) is processed
     // first, as stage 0, through the masked register path; the whole stages
-    // follow, all copied by DMA.  Summation order over K is immaterial.
+    // follow, all copied by DMA.  Summation order over K is immaterial.  Both
+    // K groups process nst stages (group 0's count; group 1's share is at most
+    // 8 shorter, so it is short of it by at most one whole stage, which then
+    // becomes its tail with no valid K: zeros).
     const int nfull = klen / kBK3;                // whole stages
-    const int has_tail = (klen % kBK3) != 0;
-    const int nst = nfull + has_tail;             // stages processed
+    const int nst = (klen0 + kBK3 - 1) / kBK3;    // stages processed
+    const int has_tail = nst - nfull;             // 0 or 1
     OpA oa;
     OpB ob;
     oa.init((const uint16_t *)p.A, p.lda, p.rows_a, m0, kbeg, wave, lane);
@@ -455,31 +477,64 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
     }
 
     // ---- epilogue: lane holds C[m][n .. n+3] of every 16 x 16 block
-    if constexpr (BM * BN * 4 <= S * STAGE) {
+    if constexpr (KG == 2) {
+        // group 1's sums join group 0's: each wave of group 1 parks its
+        // accumulators in LDS (16 bytes per lane, lane-linear: no bank
+        // conflicts) and the wave of group 0 with the same sub-tile adds them
+        static_assert(NW * FM * FN * 1024 <= LDS_BYTES, "reduction area");
+        f32x4 *xs = (f32x4 *)lds_all + wave * (FM * FN * 64) + lane;
+        __syncthreads();   // every wave's last fragment reads are done
+        if (kgrp == 1) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    xs[(i * FN + j) * 64] = acc[i][j];
+        }
+        __syncthreads();
+        if (kgrp == 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const f32x4 v = xs[(i * FN + j) * 64];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j][e] += v[e];
+                }
+        }
+    }
+    // From here on the sums are group 0's; every wave of the workgroup meets
+    // the barriers of the LDS-staged stores (their branches depend on kernel
+    // arguments only), and group 1 leaves before the direct stores.
+    if constexpr (BM * BN * 4 <= LDS_BYTES) {
         if (p.splits > 1) {
             // this split's float32 partial through LDS, like the 16-bit C below:
             // a row-major BM x BN tile (chunk q of row r at q ^ (r & 15), rows of
             // 16 or 32 chunks), then rows of 16-byte chunks per lane
             constexpr int CH = BN / 4;
             static_assert(CH >= 16, "float32 staging: rows of 16 or more chunks");
-            char *ct = lds;
+            char *ct = lds_all;
             __syncthreads();   // every wave's last fragment reads are done
+            if (kgrp == 0) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int r = wm * WM + i * 16 + fr;
-                    const int q = (wn * WN + j * 16) / 4 + fg;
-                    *(f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4)) = acc[i][j];
-                }
+                    for (int j = 0; j < FN; ++j) {
+                        const int r = wm * WM + i * 16 + fr;
+                        const int q = (wn * WN + j * 16) / 4 + fg;
+                        *(f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4)) = acc[i][j];
+                    }
+            }
             __syncthreads();
             float *W = p.ws + (int64_t)z * p.M * p.N;
             const bool wvec = (p.N & 3) == 0;
             constexpr int RPI = 64 / CH;                     // rows per read instruction
-            constexpr int RW = BM / NW;                      // tile rows per wave
+            constexpr int RW = BM / NWALL;                   // tile rows per wave
+            static_assert(RW % RPI == 0, "whole read instructions per wave");
 #pragma unroll
             for (int it = 0; it < RW / RPI; ++it) {
-                const int r = wave * RW + it * RPI + lane / CH, q = lane % CH;
+                const int r = wave_all * RW + it * RPI + lane / CH, q = lane % CH;
                 const f32x4 v = *(const f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4));
                 const int m = m0 + r, n = n0 + 4 * q;
                 if (m < p.M && n < p.N) {
@@ -500,6 +555,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
         }
     }
     if (p.splits > 1) {
+        if (kgrp != 0)
+            return;
         float *W = p.ws + (int64_t)z * p.M * p.N;
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
@@ -529,37 +586,39 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
     // low four bits for rows of 16 or 32 chunks, of bits 1..3 for rows of 8
     // (two such rows share one pass over the 64 banks), so the 8-byte writes
     // and the 16-byte reads are both free of bank conflicts.
-    if constexpr (Tr::kBytes == 2 && BM * BN * 2 <= S * STAGE) {
+    if constexpr (Tr::kBytes == 2 && BM * BN * 2 <= LDS_BYTES) {
         if (p.oe.beta == 0.0f) {
             constexpr int CH = BN / 8;                       // 16-byte chunks per row
             auto sw = [](int r) { return CH >= 16 ? (r & 15) : ((r >> 1) & 7); };
-            char *ct = lds;
+            char *ct = lds_all;
             __syncthreads();   // every wave's last fragment reads are done
+            if (kgrp == 0) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int r = wm * WM + i * 16 + fr;
-                    const int c = wn * WN + j * 16 + 4 * fg;
-                    T o[4];
+                    for (int j = 0; j < FN; ++j) {
+                        const int r = wm * WM + i * 16 + fr;
+                        const int c = wn * WN + j * 16 + 4 * fg;
+                        T o[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        o[e] = Tr::from_f32(out_value(p.oe, acc[i][j][e], 0.0f));
-                    u32x2 w;
-                    w[0] = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
-                    w[1] = (uint32_t)__builtin_bit_cast(uint16_t, o[2]) |
-                           ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
-                    *(u32x2 *)(ct + r * (BN * 2) + (((c >> 3) ^ sw(r)) << 4) + ((c >> 2) & 1) * 8) = w;
-                }
+                        for (int e = 0; e < 4; ++e)
+                            o[e] = Tr::from_f32(out_value(p.oe, acc[i][j][e], 0.0f));
+                        u32x2 w;
+                        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
+                        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, o[2]) |
+                               ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
+                        *(u32x2 *)(ct + r * (BN * 2) + (((c >> 3) ^ sw(r)) << 4) + ((c >> 2) & 1) * 8) = w;
+                    }
+            }
             __syncthreads();
             const bool vec8 = (((uintptr_t)p.C) & 15) == 0 && (p.ldc & 7) == 0;
-            constexpr int NWAVE = WGM * WGN;
             constexpr int RPI = 64 / CH;                     // rows per read instruction
-            constexpr int RW = BM / NWAVE;                   // tile rows per wave
+            constexpr int RW = BM / NWALL;                   // tile rows per wave
+            static_assert(RW % RPI == 0, "whole read instructions per wave");
 #pragma unroll
             for (int it = 0; it < RW / RPI; ++it) {
-                const int r = wave * RW + it * RPI + lane / CH, q = lane % CH;
+                const int r = wave_all * RW + it * RPI + lane / CH, q = lane % CH;
                 const u32x4 v = *(const u32x4 *)(ct + r * (BN * 2) + ((q ^ sw(r)) << 4));
                 const int m = m0 + r, n = n0 + 8 * q;
                 if (m < p.M && n < p.N) {
@@ -579,6 +638,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void mfma_gemm3_kernel(MfmaArgs p)
             return;
         }
     }
+    if (kgrp != 0)
+        return;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * WM + i * 16 + fr;

@@ -33,9 +33,13 @@ namespace tg {
 // 2304 x N x 4096 for N = 1536 .. 2560, 1024 x 1024 x 4096,
 // 512 x 512 x 16384, 256 x 256 x 65536; float32 256^3 and 512^3): the small
 // tiles need two or three workgroups per CU to hide their load latency.
+// The two-group 128 x 128 kernel (eight waves, one workgroup per CU) keeps a K
+// split of two on the CU: measured at 2304 x 1536..1792 x 4096, one workgroup
+// per tile, it sustains 0.375 of a CU's peak.
 static const TileSpec kTiles16[] = {
     {256, 256, 0.50, 160, 1.0}, {192, 256, 0.42, 140, 1.0}, {256, 128, 0.355, 96, 1.0},
-    {128, 128, 0.385, 64, 2.0}, {128, 64, 0.31, 48, 2.5},   {64, 64, 0.22, 32, 2.0},
+    {128, 128, 0.385, 64, 2.0}, {128, 128, 0.375, 128, 1.0, 2},
+    {128, 64, 0.31, 48, 2.5},   {64, 64, 0.22, 32, 2.0},
 };
 // float32: 256 x 256 is the ping-pong kernel, K-contiguous A and B only
 // (tile_fits); the smaller tiles are the register-staged kernel.  Measured at
@@ -68,20 +72,21 @@ static bool tile_fits(const Problem &p, int bm, int bn)
     return true;
 }
 
-static const TileSpec *find_tile(int dtype, int bm, int bn)
+static const TileSpec *find_tile(int dtype, int bm, int bn, int kg = 1)
 {
     const TileSpec *t;
     int n = tile_menu(dtype, &t);
     for (int i = 0; i < n; ++i)
-        if (t[i].bm == bm && t[i].bn == bn)
+        if (t[i].bm == bm && t[i].bn == bn && t[i].kg == kg)
             return &t[i];
     return nullptr;
 }
 
-int model_occupancy(int dtype, int bm, int bn, bool vec)
+int model_occupancy(int dtype, int bm, int bn, bool vec, int kg)
 {
     (void)vec;
-    const int lds_kib = 2 * (bm + bn) * 128 / 1024;
+    kg = std::max(1, kg);
+    const int lds_kib = kg * 2 * (bm + bn) * 128 / 1024;
     int by_lds = 160 / std::max(1, lds_kib);
     // register-limited residency (waves per SIMD) of each tile's wave sub-tile
     int by_regs;
@@ -96,6 +101,7 @@ int model_occupancy(int dtype, int bm, int bn, bool vec)
         by_regs = 3;
     else
         by_regs = 4;
+    by_regs /= kg;   // each K group is a full set of waves
     return std::max(1, std::min(by_lds, by_regs));
 }
 
@@ -236,7 +242,7 @@ static int plan_gemv(const Problem &p, const Chip &chip, const tg_options *opts,
 // ---------------------------------------------------------------- macro tiles
 
 struct Cand {
-    int bm, bn, s, occ, kps;
+    int bm, bn, s, occ, kps, kg;
     int64_t tiles, units, waves;
     double t, eff;
 };
@@ -246,6 +252,7 @@ static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int
 {
     Cand c{};
     const int BK = 8 * chunk_elems(p.dtype);
+    c.kg = 1;
     c.bm = bm;
     c.bn = bn;
     c.occ = occ;
@@ -342,6 +349,12 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
         menu = &generic;
         nmenu = 1;
     }
+    // K groups asked for: 0 = any offered (one when the tile is forced), 1 or 2
+    const int kg_req = opts ? opts->k_groups : 0;
+    if (kg_req == 2 && !vec) {
+        *why = "two K groups need operands the 128-bit-load kernels read";
+        return TG_ERR_UNSUPPORTED;
+    }
     // forced tile
     TileSpec forced{};
     if (opts && (opts->tile_m > 0 || opts->tile_n > 0)) {
@@ -349,18 +362,20 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
             *why = "a forced tile needs both tile_m and tile_n";
             return TG_ERR_ARG;
         }
-        const TileSpec *f = vec ? find_tile(p.dtype, opts->tile_m, opts->tile_n) : nullptr;
+        const int kg = kg_req == 2 ? 2 : 1;
+        const TileSpec *f = vec ? find_tile(p.dtype, opts->tile_m, opts->tile_n, kg) : nullptr;
         if (f && !tile_fits(p, f->bm, f->bn))
             f = nullptr;
         if (!vec && opts->tile_m == 64 && opts->tile_n == 64)
             f = &generic;
         if (!f) {
             if (!model) {
-                *why = "no macro-tile kernel of the forced size for these operands";
+                *why = kg == 2 ? "no two-K-group kernel of the forced size for these operands"
+                               : "no macro-tile kernel of the forced size for these operands";
                 return TG_ERR_UNSUPPORTED;
             }
             // the model prices any tile (e.g. another chip's tile menu)
-            forced = TileSpec{opts->tile_m, opts->tile_n, 1.0, 0, 1.0};
+            forced = TileSpec{opts->tile_m, opts->tile_n, 1.0, 0, 1.0, kg};
             f = &forced;
         }
         menu = f;
@@ -395,21 +410,22 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
     // offered (not forced) only where each tile is shared by at most eight
     // workgroups: more pieces per tile cost more in the fix-up than they save
     const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if (tile_256 && !(opts && opts->split_k > 0) && sk_ok(p, chip) &&
+    if (tile_256 && !(opts && opts->split_k > 0) && kg_req != 2 && sk_ok(p, chip) &&
         (force_sk || tiles256 * 8 >= chip.num_cus)) {
         best = price_sk(p, chip, find_tile(p.dtype, 256, 256)->eff);
         have = true;
     }
     for (int i = 0; i < nmenu && !force_sk; ++i) {
         const TileSpec &ts = menu[i];
-        if (!tile_fits(p, ts.bm, ts.bn))
+        if (!tile_fits(p, ts.bm, ts.bn) || (kg_req > 0 && ts.kg != kg_req))
             continue;
         int occ = occupancy > 0 ? occupancy
-                                : (occ_fn ? occ_fn(p.dtype, p.trans, ts.bm, ts.bn, vec, occ_ctx)
-                                          : model_occupancy(p.dtype, ts.bm, ts.bn, vec));
+                                : (occ_fn ? occ_fn(p.dtype, p.trans, ts.bm, ts.bn, vec, ts.kg, occ_ctx)
+                                          : model_occupancy(p.dtype, ts.bm, ts.bn, vec, ts.kg));
         occ = std::max(1, occ);
         for (int j = 0; j < nsplit; ++j) {
             Cand c = price(p, chip, ts.bm, ts.bn, splits[j], occ, ts.eff, ts.sat);
+            c.kg = ts.kg;
             if (!have) {
                 best = c;
                 have = true;
@@ -427,11 +443,16 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
             }
         }
     }
+    if (!have) {
+        *why = kg_req == 2 ? "no two-K-group kernel for these operands" : "no macro-tile kernel for these operands";
+        return TG_ERR_UNSUPPORTED;
+    }
     out->path = TG_PATH_MFMA;
     out->tile_m = best.bm;
     out->tile_n = best.bn;
     out->tile_k = BK;
     out->split_k = best.s;
+    out->k_groups = best.s == TG_SPLIT_STREAM_K ? 1 : best.kg;
     out->occupancy = best.occ;
     out->vector_io = vec ? 1 : 0;
     out->tiles = best.tiles;
@@ -681,6 +702,11 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
     static const char *none = "";
     *why = none;
     *out = tg_plan{};
+    out->k_groups = 1;
+    if (opts && (opts->k_groups < 0 || opts->k_groups > 2)) {
+        *why = "k_groups must be 0, 1 or 2";
+        return TG_ERR_ARG;
+    }
     if (p.M < 0 || p.N < 0 || p.K < 0) {
         *why = "negative dimension";
         return TG_ERR_ARG;
@@ -735,7 +761,8 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
             *out = direct;
         return rc_d;
     }
-    const bool tile_forced = opts && (opts->tile_m > 0 || opts->tile_n > 0);
+    // a forced tile or two K groups ask for the macro-tile kernel
+    const bool tile_forced = opts && (opts->tile_m > 0 || opts->tile_n > 0 || opts->k_groups == 2);
     const bool skinny_ok = kSkinnyEnabled &&
                            ((!opts || opts->path == TG_PATH_AUTO) ? !tile_forced : opts->path == TG_PATH_SKINNY);
     const double ridge = chip_peak(chip, p.dtype) / (chip.hbm_gbs * 1e9);
@@ -787,8 +814,12 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
         *why = "";
     }
     int path = opts ? opts->path : TG_PATH_AUTO;
-    if (path == TG_PATH_AUTO && opts && (opts->tile_m > 0 || opts->tile_n > 0))
+    if (path == TG_PATH_AUTO && tile_forced)
         path = TG_PATH_MFMA;  // a forced macro tile means the macro-tile kernel
+    if (path != TG_PATH_MFMA && path != TG_PATH_AUTO && opts && opts->k_groups == 2) {
+        *why = "two K groups exist on the macro-tile path only";
+        return TG_ERR_UNSUPPORTED;
+    }
     if (path == TG_PATH_AUTO) {
         if (p.M == 1 || p.N == 1)
             path = TG_PATH_GEMV;

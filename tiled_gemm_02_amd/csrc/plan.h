@@ -40,13 +40,15 @@ struct TileSpec {
     int lds_kib;     // LDS per workgroup (2 stages)
     double sat;      // workgroups one CU needs at once to sustain eff (a lone small
                      // tile cannot hide its own load latency)
+    int kg = 1;      // K groups: 2 = two sets of waves per workgroup, each over half of
+                     // the workgroup's K range, their sums added in LDS
 };
 
 int tile_menu(int dtype, const TileSpec **out);       // vector-load tiles, largest first
 
 // Residency of a tile kernel on one CU when no measured value is given:
 // limited by LDS (160 KiB per CU) and the kernels' register use.
-int model_occupancy(int dtype, int bm, int bn, bool vec);
+int model_occupancy(int dtype, int bm, int bn, bool vec, int kg = 1);
 
 // Skinny kernel geometry (N <= kSkinnyMaxN): a workgroup covers 64 rows and
 // all columns (64 or 128); K is split until the row blocks fill the CUs.
@@ -59,7 +61,7 @@ constexpr bool kSkinnyEnabled = true;
 
 // Occupancy lookup: returns workgroups per CU for a tile kernel; the device
 // path fills this from the runtime, the model from model_occupancy().
-typedef int (*OccFn)(int dtype, int trans, int bm, int bn, bool vec, void *ctx);
+typedef int (*OccFn)(int dtype, int trans, int bm, int bn, bool vec, int kg, void *ctx);
 
 // Plan one call.  occupancy > 0 forces that residency for every kernel.
 // Returns TG_OK or a tg_status; `why` receives a static description on error.
