@@ -129,10 +129,11 @@ typedef struct tg_options {
     int32_t split_k; /* 0 = planner's choice, 1 = no split, s > 1 = split K s ways,
                         TG_SPLIT_STREAM_K = stream-K */
     int32_t k_groups; /* macro-tile path: 0 = planner's choice (1 when the tile is
-                         forced), 1 = one group of waves per workgroup, 2 = two groups
-                         of waves per workgroup, each taking half of the workgroup's K
-                         range, summed in LDS (16-bit 128 x 128 tiles); other values
-                         are TG_ERR_ARG, 2 where no such kernel exists TG_ERR_UNSUPPORTED */
+                         forced), 1 = one group of waves per workgroup, 2 or 4 = that many
+                         groups of waves per workgroup, each taking a consecutive part of
+                         the workgroup's K range, their sums added in LDS (16-bit 128 x 128
+                         tiles: 2; float32 128 x 128: 2, 64 x 64: 4); other values are
+                         TG_ERR_ARG, a count no kernel offers TG_ERR_UNSUPPORTED */
 } tg_options;
 
 /* What the planner decided, and the quantization figures behind it. */

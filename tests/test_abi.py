@@ -141,3 +141,13 @@ def test_every_planned_16bit_tile_has_kernels(dtype):
     for bm in (256, 192):
         found = set(re.findall(rf"tg::mfma_pingpong_kernel<tg::{dtype}, \d, 16, (\w+), (\w+), false, {bm}>", stubs))
         assert len(found) == (4 if bm == 256 else 2), (bm, found)
+
+
+def test_every_planned_f32_register_tile_has_kernels():
+    """The float32 register-staged tiles the planner may pick (128 x 128 with one
+    or two K groups, 64 x 64 with one or four) exist for all four layouts."""
+    import re
+    stubs = _kernel_stubs()
+    for bm, kg in [(128, 1), (128, 2), (64, 1), (64, 4)]:
+        found = set(re.findall(rf"tg::mfma_gemm_kernel<tg::F32, {bm}, {bm}, (\w+), (\w+), true, {kg}>", stubs))
+        assert len(found) == 4, (bm, kg, found)

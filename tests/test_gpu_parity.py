@@ -242,11 +242,12 @@ def test_two_k_groups(case):
 
 
 def test_two_k_groups_refused_where_no_kernel_exists():
-    """float32, tiles other than 128 x 128, the GEMV and skinny paths and
-    operands off the 16-byte grid have no two-group kernel: the call fails;
-    k_groups = 3 is an argument error."""
+    """Four groups for 16-bit, two for the float32 256 x 256 tile, 16-bit tiles
+    other than 128 x 128, the GEMV path and operands off the 16-byte grid have
+    no K-group kernel: the call fails; k_groups = 3 is an argument error."""
     import tiled_gemm_02_amd as tg
-    for dtype, shape, opts in [(F32, (256, 256, 256), dict(k_groups=2)),
+    for dtype, shape, opts in [(F16, (256, 256, 256), dict(k_groups=4)),
+                               (F32, (256, 256, 256), dict(tile_m=256, tile_n=256, k_groups=2)),
                                (F16, (256, 256, 256), dict(tile_m=256, tile_n=256, k_groups=2)),
                                (F16, (1, 256, 256), dict(path=tg.TG_PATH_GEMV, k_groups=2)),
                                (F16, (300, 282, 130), dict(k_groups=2))]:
@@ -275,6 +276,38 @@ def test_two_k_groups_planned_and_sampled():
     assert r["ok"], r
     r = check_sampled(p, options=dict(tile_m=128, tile_n=128, split_k=2, k_groups=1))
     assert r["ok"], r
+
+
+# float32 on the register-staged kernel with K groups (64 x 64 with four,
+# 128 x 128 with two; each group over consecutive 32-deep K steps, a group past
+# the end of K loading zeros): every layout, ragged K, groups with no K, K splits,
+# alpha / beta and the epilogue
+F32_KG_CASES = [
+    (256, 256, 256, NN, 64, 4, 1, None, 1.0, 0.0),
+    (200, 136, 72, NT, 64, 4, 1, None, 1.0, 0.0),      # 3 steps over 4 groups
+    (96, 160, 8, TN, 64, 4, 1, None, 1.0, 0.0),        # one step, three empty groups
+    (264, 520, 1000, TT, 64, 4, 2, "leaky_relu", 0.5, -1.0),
+    (520, 264, 1028, NN, 128, 2, 1, None, 1.0, 0.0),
+    (264, 520, 100, NT, 128, 2, 1, "leaky_relu", 1.0, 0.0),
+    (128, 128, 4, TN, 128, 2, 1, None, -1.25, 0.75),   # K = 4: group 1 empty
+    (520, 264, 2000, TT, 128, 2, 3, None, 1.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", F32_KG_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-t{c[3]}-{c[4]}k{c[5]}s{c[6]}")
+def test_f32_k_groups(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, trans, tile, kg, split, epi, alpha, beta = case
+    _say("case f32 K groups", case)
+    p = make_problem(M, N, K, F32, trans, "normal", seed=43)
+    opts = dict(tile_m=tile, tile_n=tile, split_k=split, k_groups=kg)
+    pl = tg.tg_gemm_plan(M, N, K, F32, trans, options=opts)
+    assert pl["k_groups"] == kg and pl["split_k"] == split and pl["vector_io"] == 1, pl
+    if alpha == 1.0 and beta == 0.0:
+        r, _, _ = check_full(p, epilogue=epi, options=opts)
+    else:
+        r, _, _ = check_scaled(p, alpha, beta, epilogue=epi, options=opts)
+    assert r["ok"], (case, r)
 
 
 # float32 on the 256 x 256 ping-pong kernel: ragged M and N edges, a K tail

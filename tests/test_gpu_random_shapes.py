@@ -4,7 +4,8 @@ Fixed lists of cases drawn from two seeds: sizes from 1 to 700 in every
 dimension (aligned and not, so the vector, padded-copy and element-wise loads
 all occur), every storage type and layout, padded leading dimensions, the
 LeakyReLU epilogue, alpha / beta, and forced K splits or tiles where the
-operands allow them; and 16-bit narrow, few-row and ragged products; and 128 x 128 tiles with two K groups.  Every
+operands allow them; and 16-bit narrow, few-row and ragged products; and tiles with K groups (16-bit 128 x 128 with two,
+float32 64 x 64 with four and 128 x 128 with two).  Every
 output element is compared with the oracle.
 """
 from __future__ import annotations
@@ -125,6 +126,27 @@ def _cases_two_k_groups(n=40, seed=2026):
 
 
 CASES += _cases_two_k_groups()
+
+
+def _cases_f32_k_groups(n=24, seed=2027):
+    """float32 on the register-staged kernel with K groups (64 x 64 with four,
+    128 x 128 with two): every layout, M, N and K on the 16-byte grid from 4 to
+    1200 (K down to one step, so some groups get no K), outer K splits 1 to 3."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        trans = [NN, NT, TN, TT][int(rng.integers(0, 4))]
+        tile, kg = [(64, 4), (128, 2)][int(rng.integers(0, 2))]
+        M, N, K = (int(rng.integers(1, 301)) * 4 for _ in range(3))
+        split = int(rng.integers(1, 4)) if K >= 256 else 1
+        epi = "leaky_relu" if rng.random() < 0.3 else None
+        scaled = rng.random() < 0.3
+        out.append((400 + i, M, N, K, F32, trans, 0, epi, scaled,
+                    dict(tile_m=tile, tile_n=tile, split_k=split, k_groups=kg)))
+    return out
+
+
+CASES += _cases_f32_k_groups()
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-d{c[4]}-t{c[5]}")

@@ -178,15 +178,33 @@ def test_two_k_group_plans():
     # other paths report one group
     assert tg.tg_plan_model(1, 8192, 8192, F)["k_groups"] == 1
     assert tg.tg_plan_model(8192, 128, 8192, F)["k_groups"] == 1
-    # no two-group kernel: float32, other tiles, other paths, off-grid operands; bad values
-    for args, opts in [((1024, 1024, 4096, tg.TG_F32), dict(k_groups=2)),
+    # no such kernel: four groups for 16-bit, stream-K, other paths, off-grid operands;
+    # bad values (a forced tile the model prices whatever it is)
+    for args, opts in [((1024, 1024, 4096, F), dict(k_groups=4)),
                        ((1024, 1024, 4096, F), dict(k_groups=2, split_k=tg.TG_SPLIT_STREAM_K)),
                        ((1, 1024, 4096, F), dict(k_groups=2, path=tg.TG_PATH_GEMV)),
                        ((300, 282, 130, F), dict(k_groups=2)),
                        ((1024, 1024, 4096, F), dict(k_groups=3)),
+                       ((1024, 1024, 4096, F), dict(k_groups=8)),
                        ((1024, 1024, 4096, F), dict(k_groups=-1))]:
         with pytest.raises(tg.TgError):
             tg.tg_plan_model(*args, tg.TG_NN, options=opts)
+
+
+def test_f32_k_group_plans():
+    """float32 on the register-staged kernel with K groups: 64 x 64 with four
+    groups where few tiles meet a long K (1024^3: 256 tiles, one workgroup of
+    sixteen waves each), 128 x 128 with two where the tiles fill the CUs once
+    (2048^3); the 256 x 256 ping-pong tile and large products keep one group."""
+    F = tg.TG_F32
+    p = tg.tg_plan_model(1024, 1024, 1024, F)
+    assert (p["tile_m"], p["k_groups"], p["split_k"], p["workspace_bytes"]) == (64, 4, 1, 0), p
+    p = tg.tg_plan_model(2048, 2048, 2048, F)
+    assert (p["tile_m"], p["k_groups"], p["split_k"]) == (128, 2, 1), p
+    p = tg.tg_plan_model(8192, 8192, 8192, F, tg.TG_NT)
+    assert (p["tile_m"], p["k_groups"]) == (256, 1), p
+    f = tg.tg_plan_model(256, 256, 256, F, options=dict(tile_m=64, tile_n=64, k_groups=4, split_k=1))
+    assert (f["k_groups"], f["workgroups"], f["occupancy"]) == (4, 16, 1), f
 
 
 def test_stream_k_plans():

@@ -20,13 +20,13 @@ namespace tg {
 
 // ---------------------------------------------------------------- dispatch by type
 
-hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, const MfmaArgs &a,
+hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, int kg, const MfmaArgs &a,
                        hipStream_t s)
 {
     switch (dtype) {
-    case TG_F16: return launch_mfma_f16(trans, bm, bn, vec, a, s);
-    case TG_BF16: return launch_mfma_bf16(trans, bm, bn, vec, a, s);
-    case TG_F32: return launch_mfma_f32(trans, bm, bn, vec, a, s);
+    case TG_F16: return launch_mfma_f16(trans, bm, bn, vec, kg, a, s);
+    case TG_BF16: return launch_mfma_bf16(trans, bm, bn, vec, kg, a, s);
+    case TG_F32: return launch_mfma_f32(trans, bm, bn, vec, kg, a, s);
     }
     return hipErrorInvalidValue;
 }
@@ -78,12 +78,12 @@ static bool use_mfma2(int dtype, int trans, bool vec, int bm, int bn, int64_t ld
     return true;
 }
 
-int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec)
+int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec, int kg)
 {
     switch (dtype) {
-    case TG_F16: return mfma_occupancy_f16(trans, bm, bn, vec);
-    case TG_BF16: return mfma_occupancy_bf16(trans, bm, bn, vec);
-    case TG_F32: return mfma_occupancy_f32(trans, bm, bn, vec);
+    case TG_F16: return mfma_occupancy_f16(trans, bm, bn, vec, kg);
+    case TG_BF16: return mfma_occupancy_bf16(trans, bm, bn, vec, kg);
+    case TG_F32: return mfma_occupancy_f32(trans, bm, bn, vec, kg);
     }
     return 0;
 }
@@ -214,8 +214,8 @@ struct DeviceInfo {
     // device address of this device's copy of `scratch` (tg_gemm_noalloc),
     // taken once with this device current; null until then
     void *scratch_ptr = nullptr;
-    // measured residency per (dtype, trans, tile, vec), 0 = not yet asked
-    int occ[3][4][8][2][2] = {};   // dtype, trans, tile, vector loads, K groups - 1
+    // measured residency per (dtype, trans, tile, vec, K groups 1 / 2 / 4), 0 = not yet asked
+    int occ[3][4][8][2][3] = {};
     // benchmark-mode winners (tg_autotune) per problem, used by calls that
     // pass no options; guarded by g_tune_mu
     std::map<TuneKey, tg_options> tuned;
@@ -317,14 +317,14 @@ static int device_occ(int dtype, int trans, int bm, int bn, bool vec, int kg, vo
 {
     DeviceInfo *d = (DeviceInfo *)ctx;
     const int ts = tile_slot(bm, bn);
-    if (ts < 0 || kg < 1 || kg > 2)
+    const int ki = kg == 1 ? 0 : kg == 2 ? 1 : kg == 4 ? 2 : -1;
+    if (ts < 0 || ki < 0)
         return model_occupancy(dtype, bm, bn, vec, kg);
     std::lock_guard<std::mutex> lk(g_dev_mu);
-    int &slot = d->occ[dtype][trans][ts][vec ? 1 : 0][kg - 1];
+    int &slot = d->occ[dtype][trans][ts][vec ? 1 : 0][ki];
     if (slot == 0) {
         int n = use_mfma2(dtype, trans, vec, bm, bn, 0, 0) ? mfma2_occupancy(dtype, trans, bm, bn, kg)
-                : kg == 1                                   ? mfma_occupancy(dtype, trans, bm, bn, vec)
-                                                            : 0;
+                                                           : mfma_occupancy(dtype, trans, bm, bn, vec, kg);
         slot = n > 0 ? n : -1;
     }
     return slot > 0 ? slot : model_occupancy(dtype, bm, bn, vec, kg);
@@ -465,13 +465,10 @@ static int run_plan(const tg_plan &pl, const Problem &p, const void *A, const vo
         a.splits = pl.split_k;
         if (pl.vector_io != 0 && p.dtype != TG_F32 && (p.lda > kDmaMaxLd16 || p.ldb > kDmaMaxLd16))
             return fail(TG_ERR_UNSUPPORTED, "16-bit vector-load plan with a leading dimension above 2^22");
-        const bool dma = use_mfma2(p.dtype, p.trans, pl.vector_io != 0, pl.tile_m, pl.tile_n, p.lda, p.ldb);
-        if (pl.k_groups != 1 && !dma)
-            return fail(TG_ERR_UNSUPPORTED, "a plan with %d K groups needs the LDS-DMA kernels", pl.k_groups);
-        if (dma)
+        if (use_mfma2(p.dtype, p.trans, pl.vector_io != 0, pl.tile_m, pl.tile_n, p.lda, p.ldb))
             e = launch_mfma2(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.k_groups, a, s);
         else
-            e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, a, s);
+            e = launch_mfma(p.dtype, p.trans, pl.tile_m, pl.tile_n, pl.vector_io != 0, pl.k_groups, a, s);
         if (e == hipSuccess && pl.split_k > 1)
             e = launch_splitk_reduce(p.dtype, (const float *)ws, pl.split_k, p.N, p.M * p.N, (int)p.M, (int)p.N, C,
                                      p.ldc, oe, a.c_vec, s);

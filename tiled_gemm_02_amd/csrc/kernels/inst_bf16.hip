@@ -9,6 +9,8 @@
 // 16-bit vector loads run on the LDS-DMA kernels only: the register-staged
 // kernel keeps its element-wise 64 x 64 form for operands off the 16-byte grid
 #define TG_REG_TILE_LIST
+// of those, the ones also built with K groups per workgroup (tile, groups)
+#define TG_REG_KG_TILE_LIST
 #define TG_HAS_MFMA2 1
 #define TG_HAS_SKINNY 1
 #include "instances.inc"

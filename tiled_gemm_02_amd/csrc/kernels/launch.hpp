@@ -12,11 +12,12 @@
 
 namespace tg {
 
-// hipErrorInvalidValue: no instance for this (type, tile, load width).
-hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, const MfmaArgs &a,
+// The register-staged kernel; kg = K groups per workgroup.  hipErrorInvalidValue:
+// no instance for this (type, tile, load width, K groups).
+hipError_t launch_mfma(int dtype, int trans, int bm, int bn, bool vec, int kg, const MfmaArgs &a,
                        hipStream_t s);
 // Resident workgroups per CU of an instance (0 if none).
-int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec);
+int mfma_occupancy(int dtype, int trans, int bm, int bn, bool vec, int kg);
 // The LDS-DMA kernel for 16-bit, 16-byte-aligned operands (same tiles); kg = K
 // groups per workgroup (1, or 2 for the tiles built with two).
 hipError_t launch_mfma2(int dtype, int trans, int bm, int bn, int kg, const MfmaArgs &a, hipStream_t s);
@@ -46,9 +47,9 @@ hipError_t launch_skinny(int dtype, bool trans_b, const SkinnyArgs &a, hipStream
 hipError_t launch_softmax(int dtype, int q, int c, bool vec, const SoftmaxArgs &a, hipStream_t s);
 
 #define TG_DECLARE_TYPE_LAUNCHERS(NAME)                                                          \
-    hipError_t launch_mfma_##NAME(int trans, int bm, int bn, bool vec, const MfmaArgs &a,        \
+    hipError_t launch_mfma_##NAME(int trans, int bm, int bn, bool vec, int kg, const MfmaArgs &a, \
                                   hipStream_t s);                                                \
-    int mfma_occupancy_##NAME(int trans, int bm, int bn, bool vec);                              \
+    int mfma_occupancy_##NAME(int trans, int bm, int bn, bool vec, int kg);                      \
     hipError_t launch_splitk_reduce_##NAME(const float *ws, int splits, int64_t wsld,            \
                                            int64_t plane, int M, int N, void *C, int64_t ldc,    \
                                            OutEpi oe, int c_vec, hipStream_t s);                 \

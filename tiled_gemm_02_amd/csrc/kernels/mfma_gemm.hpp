@@ -31,6 +31,14 @@
 // M and N edges clamp the row index (rows past the edge are computed but never
 // stored); the last partial K step is zero-filled; split-K writes float32
 // partial tiles that a separate pass reduces in a fixed order.
+//
+// K groups (KG = 2 or 4): the workgroup holds KG sets of the four waves, each
+// with its own two LDS stages, taking consecutive runs of ceil(steps / KG)
+// BK-deep steps of the workgroup's K range; every group runs the same number of
+// steps (they share the barriers), loads past the end of its run being
+// zero-filled like any K tail.  Groups 1 .. KG-1 then park their sums in LDS
+// and group 0 adds them in group order (a fixed order) and stores the tile: a
+// split of K whose reduction stays on the CU.
 #pragma once
 
 #include "common.hpp"
@@ -205,8 +213,8 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
     tn = in / gs;
 }
 
-template <typename Tr, int BM, int BN, bool TA, bool TB, bool VEC>
-__global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs p)
+template <typename Tr, int BM, int BN, bool TA, bool TB, bool VEC, int KG = 1>
+__global__ __launch_bounds__(256 * KG) void mfma_gemm_kernel(MfmaArgs p)
 {
     using T = typename Tr::T;
     constexpr int E = Tr::E;
@@ -214,10 +222,13 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs p)
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int FM = WM / 16, FN = WN / 16;
     constexpr int STAGE = (BM + BN) * 8;  // 16-byte chunks per stage
+    static_assert(KG == 1 || KG == 2 || KG == 4, "1, 2 or 4 K groups");
 
-    __shared__ u32x4 lds[2 * STAGE];
+    __shared__ u32x4 lds_all[KG * 2 * STAGE];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;                 // thread within its K group
+    const int kgrp = threadIdx.x >> 8;                 // K group (uniform per wave)
+    u32x4 *const lds = lds_all + kgrp * (2 * STAGE);   // the group's two stages
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -226,9 +237,11 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs p)
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int z = blockIdx.y;
-    const int kbeg = z * p.kps;
-    const int kend = min(p.K, kbeg + p.kps);
-    const int nk = (kend - kbeg + BK - 1) / BK;
+    const int kbeg_wg = z * p.kps;
+    const int kend_wg = min(p.K, kbeg_wg + p.kps);
+    const int nk = ((kend_wg - kbeg_wg + BK - 1) / BK + KG - 1) / KG;   // steps per group
+    const int kbeg = kbeg_wg + kgrp * nk * BK;
+    const int kend = min(kend_wg, kbeg + nk * BK);   // below kbeg for a group with no K
 
     Stager<Tr, BM, TA, VEC> sa;
     sa.X = (const T *)p.A; sa.ld = p.lda; sa.rows_total = p.rows_a; sa.row0 = m0;
@@ -296,6 +309,35 @@ __global__ __launch_bounds__(256) void mfma_gemm_kernel(MfmaArgs p)
     }
 
     // ---- epilogue: lane holds C[m][n .. n+3] of every 16 x 16 block
+    if constexpr (KG > 1) {
+        // groups 1 .. KG-1 park their sums in LDS (16 bytes per lane, lane-
+        // linear), group 0 adds them in group order; the K loop ended with a
+        // barrier, so the stages are free
+        static_assert((KG - 1) * 4 * FM * FN * 64 <= KG * 2 * STAGE, "reduction area");
+        f32x4 *xs = (f32x4 *)lds_all;
+        auto slot = [&](int g, int i, int j) { return (((g - 1) * 4 + wave) * (FM * FN) + i * FN + j) * 64 + lane; };
+        if (kgrp > 0) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    xs[slot(kgrp, i, j)] = acc[i][j];
+        }
+        __syncthreads();
+        if (kgrp > 0)
+            return;
+#pragma unroll
+        for (int g = 1; g < KG; ++g)
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const f32x4 v = xs[slot(g, i, j)];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j][e] += v[e];
+                }
+    }
     const int fr = lane & 15, fg = lane >> 4;
     if (p.splits > 1) {
         float *W = p.ws + (int64_t)z * p.M * p.N;

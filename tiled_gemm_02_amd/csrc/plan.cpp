@@ -44,10 +44,14 @@ static const TileSpec kTiles16[] = {
 // float32: 256 x 256 is the ping-pong kernel, K-contiguous A and B only
 // (tile_fits); the smaller tiles are the register-staged kernel.  Measured at
 // 8192^3 on MI355X: 137.6 TFLOP/s (NT, 256 x 256) and 126 (NN, 128 x 128) of
-// the 157.3 TFLOP/s float32 matrix peak.
+// the 157.3 TFLOP/s float32 matrix peak.  With K groups (one workgroup per CU):
+// 128 x 128 x 2 groups at 2048^3 and 1024 x 1024 x 4096 split 4, 0.68-0.71;
+// 64 x 64 x 4 groups at 512^3 and 1024^3, 0.57.
 static const TileSpec kTiles32[] = {
     {256, 256, 0.87, 160, 1.0},
     {128, 128, 0.80, 64, 2.0},
+    {128, 128, 0.70, 128, 1.0, 2},
+    {64, 64, 0.57, 128, 1.0, 4},
     {64, 64, 0.48, 32, 2.0},
 };
 
@@ -349,10 +353,10 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
         menu = &generic;
         nmenu = 1;
     }
-    // K groups asked for: 0 = any offered (one when the tile is forced), 1 or 2
+    // K groups asked for: 0 = any offered (one when the tile is forced), 1, 2 or 4
     const int kg_req = opts ? opts->k_groups : 0;
-    if (kg_req == 2 && !vec) {
-        *why = "two K groups need operands the 128-bit-load kernels read";
+    if (kg_req > 1 && !vec) {
+        *why = "K groups need operands the 128-bit-load kernels read";
         return TG_ERR_UNSUPPORTED;
     }
     // forced tile
@@ -362,7 +366,7 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
             *why = "a forced tile needs both tile_m and tile_n";
             return TG_ERR_ARG;
         }
-        const int kg = kg_req == 2 ? 2 : 1;
+        const int kg = std::max(1, kg_req);
         const TileSpec *f = vec ? find_tile(p.dtype, opts->tile_m, opts->tile_n, kg) : nullptr;
         if (f && !tile_fits(p, f->bm, f->bn))
             f = nullptr;
@@ -370,8 +374,8 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
             f = &generic;
         if (!f) {
             if (!model) {
-                *why = kg == 2 ? "no two-K-group kernel of the forced size for these operands"
-                               : "no macro-tile kernel of the forced size for these operands";
+                *why = kg > 1 ? "no kernel of the forced size with these K groups for these operands"
+                              : "no macro-tile kernel of the forced size for these operands";
                 return TG_ERR_UNSUPPORTED;
             }
             // the model prices any tile (e.g. another chip's tile menu)
@@ -410,7 +414,7 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
     // offered (not forced) only where each tile is shared by at most eight
     // workgroups: more pieces per tile cost more in the fix-up than they save
     const int64_t tiles256 = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-    if (tile_256 && !(opts && opts->split_k > 0) && kg_req != 2 && sk_ok(p, chip) &&
+    if (tile_256 && !(opts && opts->split_k > 0) && kg_req <= 1 && sk_ok(p, chip) &&
         (force_sk || tiles256 * 8 >= chip.num_cus)) {
         best = price_sk(p, chip, find_tile(p.dtype, 256, 256)->eff);
         have = true;
@@ -444,7 +448,7 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
         }
     }
     if (!have) {
-        *why = kg_req == 2 ? "no two-K-group kernel for these operands" : "no macro-tile kernel for these operands";
+        *why = kg_req > 1 ? "no kernel with these K groups for these operands" : "no macro-tile kernel for these operands";
         return TG_ERR_UNSUPPORTED;
     }
     out->path = TG_PATH_MFMA;
@@ -703,8 +707,8 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
     *why = none;
     *out = tg_plan{};
     out->k_groups = 1;
-    if (opts && (opts->k_groups < 0 || opts->k_groups > 2)) {
-        *why = "k_groups must be 0, 1 or 2";
+    if (opts && !(opts->k_groups >= 0 && opts->k_groups <= 2) && opts->k_groups != 4) {
+        *why = "k_groups must be 0, 1, 2 or 4";
         return TG_ERR_ARG;
     }
     if (p.M < 0 || p.N < 0 || p.K < 0) {
@@ -762,7 +766,7 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
         return rc_d;
     }
     // a forced tile or two K groups ask for the macro-tile kernel
-    const bool tile_forced = opts && (opts->tile_m > 0 || opts->tile_n > 0 || opts->k_groups == 2);
+    const bool tile_forced = opts && (opts->tile_m > 0 || opts->tile_n > 0 || opts->k_groups > 1);
     const bool skinny_ok = kSkinnyEnabled &&
                            ((!opts || opts->path == TG_PATH_AUTO) ? !tile_forced : opts->path == TG_PATH_SKINNY);
     const double ridge = chip_peak(chip, p.dtype) / (chip.hbm_gbs * 1e9);
@@ -816,8 +820,8 @@ int make_plan(const Problem &p, const Chip &chip, int occupancy, const tg_option
     int path = opts ? opts->path : TG_PATH_AUTO;
     if (path == TG_PATH_AUTO && tile_forced)
         path = TG_PATH_MFMA;  // a forced macro tile means the macro-tile kernel
-    if (path != TG_PATH_MFMA && path != TG_PATH_AUTO && opts && opts->k_groups == 2) {
-        *why = "two K groups exist on the macro-tile path only";
+    if (path != TG_PATH_MFMA && path != TG_PATH_AUTO && opts && opts->k_groups > 1) {
+        *why = "K groups exist on the macro-tile path only";
         return TG_ERR_UNSUPPORTED;
     }
     if (path == TG_PATH_AUTO) {

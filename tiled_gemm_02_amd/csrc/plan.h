@@ -40,7 +40,7 @@ struct TileSpec {
     int lds_kib;     // LDS per workgroup (2 stages)
     double sat;      // workgroups one CU needs at once to sustain eff (a lone small
                      // tile cannot hide its own load latency)
-    int kg = 1;      // K groups: 2 = two sets of waves per workgroup, each over half of
+    int kg = 1;      // K groups: 2 or 4 sets of waves per workgroup, each over a part of
                      // the workgroup's K range, their sums added in LDS
 };
 
