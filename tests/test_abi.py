@@ -138,9 +138,11 @@ def test_every_planned_16bit_tile_has_kernels(dtype):
         found = set(re.findall(
             rf"tg::mfma_gemm3_kernel<tg::{dtype}, {bm}, {bn}, \d+, 2, 2, (\w+), (\w+), {kg}>", stubs))
         assert len(found) == 4, (bm, bn, kg, found)
+    # the ping-pong tiles in two forms: whole tile to C (1), K splits and old C (0)
     for bm in (256, 192):
-        found = set(re.findall(rf"tg::mfma_pingpong_kernel<tg::{dtype}, \d, 16, (\w+), (\w+), false, {bm}>", stubs))
-        assert len(found) == (4 if bm == 256 else 2), (bm, found)
+        found = set(re.findall(rf"tg::mfma_pingpong_kernel<tg::{dtype}, \d, 16, (\w+), (\w+), false, {bm}, (\d)>",
+                               stubs))
+        assert len(found) == (8 if bm == 256 else 4), (bm, found)
 
 
 def test_every_planned_f32_register_tile_has_kernels():

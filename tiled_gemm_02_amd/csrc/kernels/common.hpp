@@ -47,6 +47,13 @@ __device__ __forceinline__ float out_value(const OutEpi &oe, float acc, float c_
     return apply_epi(x, oe.kind, oe.slope);
 }
 
+// out_value where the caller knows beta is 0 (no old C): without that
+// knowledge the compiler keeps the beta term's multiply and test per element.
+__device__ __forceinline__ float out_value_no_c(const OutEpi &oe, float acc)
+{
+    return apply_epi(oe.alpha * acc, oe.kind, oe.slope);
+}
+
 // Bit reinterpretation of one 32-bit lane value.  The argument is taken by
 // value: bit-casting a vector-element expression (v[i]) directly has been seen
 // to read element 0 whatever i is, so callers copy the element out first.

@@ -602,7 +602,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
                         T o[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            o[e] = Tr::from_f32(out_value(p.oe, acc[i][j][e], 0.0f));
+                            o[e] = Tr::from_f32(out_value_no_c(p.oe, acc[i][j][e]));
                         u32x2 w;
                         w[0] = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) |
                                ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);

@@ -87,7 +87,12 @@ __device__ __forceinline__ uint32_t mn32_base(uint32_t st, int ks, int h, int la
     return st + (uint32_t)((k * CH + c) * 16 + (n & 7) * 2);
 }
 
-template <typename Tr, int S, int MI, bool TA, bool TB, bool SK = false, int BM = 256>
+// EP selects the epilogue the instance carries: 1 = the whole tile to a 16-bit
+// C without old C (no K split, beta = 0: the LDS-staged row stores and nothing
+// else), 0 = every other case (K-split partials, old C, float32).  The launcher
+// picks the instance from the call, so no kernel holds code it cannot run; the
+// unused epilogues cost the whole-tile kernel about 1 % at 8192^3 when present.
+template <typename Tr, int S, int MI, bool TA, bool TB, bool SK = false, int BM = 256, int EP = 0>
 __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -346,146 +351,147 @@ __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
         // tile, 16 bytes per lane.  The MFMA layout stores 16 rows x 32 bytes
         // per instruction instead, four times the L2 requests for the same
         // bytes, and all workgroups of a wave of tiles store at once.
-        if constexpr (!SK && MI == 16 && Tr::kBytes == 2 && BM * 512 <= S * STAGE) {
-            if (p.splits == 1 && p.oe.beta == 0.0f) {
-                // Every LDS read of the ring was consumed by an MFMA before the
-                // last barrier of the loop, and every copy had landed.  Chunk q
-                // (16 bytes) of row r sits at chunk q ^ (r & 15): the 8-byte
-                // writes below and the 16-byte reads after are bank-conflict-free.
-                char *ct = lds;
+        if constexpr (EP == 1) {
+            static_assert(!SK && MI == 16 && Tr::kBytes == 2 && BM * 512 <= S * STAGE,
+                          "the staged 16-bit epilogue needs 16 x 16 blocks and a ring of the tile's size");
+            // Every LDS read of the ring was consumed by an MFMA before the
+            // last barrier of the loop, and every copy had landed.  Chunk q
+            // (16 bytes) of row r sits at chunk q ^ (r & 15): the 8-byte
+            // writes below and the 16-byte reads after are bank-conflict-free.
+            char *ct = lds;
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < FN; ++j) {
-                        const int r = wm * WM + 16 * i + (lane & 15);
-                        const int c = wn * WN + 16 * j + 4 * (lane >> 4);
-                        T o[4];
+                for (int j = 0; j < FN; ++j) {
+                    const int r = wm * WM + 16 * i + (lane & 15);
+                    const int c = wn * WN + 16 * j + 4 * (lane >> 4);
+                    T o[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            o[e] = Tr::from_f32(out_value(p.oe, acc[i][j][e], 0.0f));
-                        u32x2 w;
-                        w[0] = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
-                        w[1] = (uint32_t)__builtin_bit_cast(uint16_t, o[2]) |
-                               ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
-                        *(u32x2 *)(ct + r * 512 + (((c >> 3) ^ (r & 15)) << 4) + ((c >> 2) & 1) * 8) = w;
-                    }
-                __syncthreads();
-                const bool vec8 = (((uintptr_t)p.C) & 15) == 0 && (p.ldc & 7) == 0;
-                constexpr int RW = BM / 8;   // tile rows per wave
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = Tr::from_f32(out_value_no_c(p.oe, acc[i][j][e]));
+                    u32x2 w;
+                    w[0] = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
+                    w[1] = (uint32_t)__builtin_bit_cast(uint16_t, o[2]) |
+                           ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
+                    *(u32x2 *)(ct + r * 512 + (((c >> 3) ^ (r & 15)) << 4) + ((c >> 2) & 1) * 8) = w;
+                }
+            __syncthreads();
+            const bool vec8 = (((uintptr_t)p.C) & 15) == 0 && (p.ldc & 7) == 0;
+            constexpr int RW = BM / 8;   // tile rows per wave
 #pragma unroll
-                for (int it = 0; it < RW / 2; ++it) {
-                    const int r = wave * RW + 2 * it + (lane >> 5), q = lane & 31;
-                    const u32x4 v = *(const u32x4 *)(ct + r * 512 + ((q ^ (r & 15)) << 4));
-                    const int m = m0 + r, n = n0 + 8 * q;
-                    if (m < p.M) {
-                        T *dst = C + (int64_t)m * p.ldc + n;
-                        if (vec8 && n + 7 < p.N) {
-                            *(u32x4 *)dst = v;
-                        } else {
+            for (int it = 0; it < RW / 2; ++it) {
+                const int r = wave * RW + 2 * it + (lane >> 5), q = lane & 31;
+                const u32x4 v = *(const u32x4 *)(ct + r * 512 + ((q ^ (r & 15)) << 4));
+                const int m = m0 + r, n = n0 + 8 * q;
+                if (m < p.M) {
+                    T *dst = C + (int64_t)m * p.ldc + n;
+                    if (vec8 && n + 7 < p.N) {
+                        *(u32x4 *)dst = v;
+                    } else {
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const uint32_t word = v[e >> 1];
-                                if (n + e < p.N)
-                                    dst[e] = __builtin_bit_cast(T, (uint16_t)(word >> (16 * (e & 1))));
-                            }
+                        for (int e = 0; e < 8; ++e) {
+                            const uint32_t word = v[e >> 1];
+                            if (n + e < p.N)
+                                dst[e] = __builtin_bit_cast(T, (uint16_t)(word >> (16 * (e & 1))));
                         }
                     }
                 }
-                return;
             }
-        }
-        // ---- K split: this split's float32 partial through LDS, one group's
-        // half of the tile (the whole ring) at a time: row-major rows of 16-byte
-        // chunks, chunk q of row r at q ^ (r & 15), then every wave stores rows
-        // of the half, 16 bytes per lane
-        if constexpr (!SK && MI == 16 && (BM / 2) * BN * 4 <= S * STAGE) {
-            if (p.splits > 1) {
-                constexpr int CH = BN / 4;      // 16-byte chunks per row
-                constexpr int RW = WM / 8;      // rows of a half per wave
-                char *ct = lds;
-                float *Wz = p.ws + (int64_t)z * p.M * p.N;
-                const bool wvec = (p.N & 3) == 0;
+            return;
+        } else {
+            // ---- K split: this split's float32 partial through LDS, one group's
+            // half of the tile (the whole ring) at a time: row-major rows of 16-byte
+            // chunks, chunk q of row r at q ^ (r & 15), then every wave stores rows
+            // of the half, 16 bytes per lane
+            if constexpr (!SK && MI == 16 && (BM / 2) * BN * 4 <= S * STAGE) {
+                if (p.splits > 1) {
+                    constexpr int CH = BN / 4;      // 16-byte chunks per row
+                    constexpr int RW = WM / 8;      // rows of a half per wave
+                    char *ct = lds;
+                    float *Wz = p.ws + (int64_t)z * p.M * p.N;
+                    const bool wvec = (p.N & 3) == 0;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    __syncthreads();   // the ring is idle (or the last half is stored)
-                    if (grp == h) {
+                    for (int h = 0; h < 2; ++h) {
+                        __syncthreads();   // the ring is idle (or the last half is stored)
+                        if (grp == h) {
 #pragma unroll
-                        for (int i = 0; i < FM; ++i)
+                            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                            for (int j = 0; j < FN; ++j) {
-                                const int r = 16 * i + (lane & 15);
-                                const int q = (wn * WN + 16 * j) / 4 + (lane >> 4);
-                                *(f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4)) = acc[i][j];
-                            }
-                    }
-                    __syncthreads();
+                                for (int j = 0; j < FN; ++j) {
+                                    const int r = 16 * i + (lane & 15);
+                                    const int q = (wn * WN + 16 * j) / 4 + (lane >> 4);
+                                    *(f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4)) = acc[i][j];
+                                }
+                        }
+                        __syncthreads();
 #pragma unroll
-                    for (int it = 0; it < RW * CH / 64; ++it) {
-                        const int r = wave * RW + (it * 64 + lane) / CH, q = (it * 64 + lane) % CH;
-                        const f32x4 v = *(const f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4));
-                        const int m = m0 + h * WM + r, n = n0 + 4 * q;
-                        if (m < p.M && n < p.N) {
-                            float *dst = Wz + (int64_t)m * p.N + n;
-                            if (wvec && n + 3 < p.N) {
-                                *(f32x4 *)dst = v;
-                            } else {
+                        for (int it = 0; it < RW * CH / 64; ++it) {
+                            const int r = wave * RW + (it * 64 + lane) / CH, q = (it * 64 + lane) % CH;
+                            const f32x4 v = *(const f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4));
+                            const int m = m0 + h * WM + r, n = n0 + 4 * q;
+                            if (m < p.M && n < p.N) {
+                                float *dst = Wz + (int64_t)m * p.N + n;
+                                if (wvec && n + 3 < p.N) {
+                                    *(f32x4 *)dst = v;
+                                } else {
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    const float x = v[e];
-                                    if (n + e < p.N)
-                                        dst[e] = x;
+                                    for (int e = 0; e < 4; ++e) {
+                                        const float x = v[e];
+                                        if (n + e < p.N)
+                                            dst[e] = x;
+                                    }
                                 }
                             }
                         }
                     }
-                }
-                return;
-            }
-        }
-        // ---- epilogue: each lane holds runs of 4 consecutive columns of C
-        float *W = p.ws + (int64_t)z * p.M * p.N;
-        auto store4 = [&](int m, int n, const f32x4 &v) {
-            if constexpr (SK) {
-                if (Wt) {   // the whole tile, rows and columns past M and N included
-                    *(f32x4 *)(Wt + (m - m0) * BN + (n - n0)) = v;
                     return;
                 }
             }
-            if (m >= p.M || n >= p.N)
-                return;
-            if (!SK && p.splits > 1) {
-                float *dst = W + (int64_t)m * p.N + n;
-                if (n + 3 < p.N && (p.N & 3) == 0) {
-                    *(f32x4 *)dst = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < p.N)
-                            dst[e] = v[e];
-                }
-                return;
-            }
-            store_out4<Tr>(C + (int64_t)m * p.ldc + n, v, p.N - n, p.c_vec && n + 3 < p.N, p.oe);
-        };
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                if constexpr (MI == 16) {
-                    // C[m0 + .. + (lane & 15)][n0 + .. + 4 (lane >> 4) .. + 3]
-                    store4(m0 + wm * WM + 16 * i + (lane & 15), n0 + wn * WN + 16 * j + 4 * (lane >> 4),
-                           acc[i][j]);
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                         acc[i][j][4 * q + 3]};
-                        store4(m0 + wm * WM + 32 * i + (lane & 31),
-                               n0 + wn * WN + 32 * j + 8 * q + 4 * (lane >> 5), v);
+            // ---- epilogue: each lane holds runs of 4 consecutive columns of C
+            float *W = p.ws + (int64_t)z * p.M * p.N;
+            auto store4 = [&](int m, int n, const f32x4 &v) {
+                if constexpr (SK) {
+                    if (Wt) {   // the whole tile, rows and columns past M and N included
+                        *(f32x4 *)(Wt + (m - m0) * BN + (n - n0)) = v;
+                        return;
                     }
                 }
-            }
+                if (m >= p.M || n >= p.N)
+                    return;
+                if (!SK && p.splits > 1) {
+                    float *dst = W + (int64_t)m * p.N + n;
+                    if (n + 3 < p.N && (p.N & 3) == 0) {
+                        *(f32x4 *)dst = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.N)
+                                dst[e] = v[e];
+                    }
+                    return;
+                }
+                store_out4<Tr>(C + (int64_t)m * p.ldc + n, v, p.N - n, p.c_vec && n + 3 < p.N, p.oe);
+            };
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (MI == 16) {
+                        // C[m0 + .. + (lane & 15)][n0 + .. + 4 (lane >> 4) .. + 3]
+                        store4(m0 + wm * WM + 16 * i + (lane & 15), n0 + wn * WN + 16 * j + 4 * (lane >> 4),
+                               acc[i][j]);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                             acc[i][j][4 * q + 3]};
+                            store4(m0 + wm * WM + 32 * i + (lane & 31),
+                                   n0 + wn * WN + 32 * j + 8 * q + 4 * (lane >> 5), v);
+                        }
+                    }
+                }
+        }
     };
 
     if constexpr (!SK) {
