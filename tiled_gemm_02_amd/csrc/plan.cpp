@@ -35,10 +35,13 @@ namespace tg {
 // tiles need two or three workgroups per CU to hide their load latency.
 // The two-group 128 x 128 kernel (eight waves, one workgroup per CU) keeps a K
 // split of two on the CU: measured at 2304 x 1536..1792 x 4096, one workgroup
-// per tile, it sustains 0.375 of a CU's peak.
+// per tile, it sustains 0.375 of a CU's peak, plus about 4 us per workgroup
+// (the reduction in LDS and both groups' fills), which decides against it for
+// short K (measured over 78 fp16 shapes x every tile and split: the picks with
+// the fixed charge average 1.009x the best candidate's time, 1.011x without).
 static const TileSpec kTiles16[] = {
     {256, 256, 0.50, 160, 1.0}, {192, 256, 0.42, 140, 1.0}, {256, 128, 0.355, 96, 1.0},
-    {128, 128, 0.385, 64, 2.0}, {128, 128, 0.375, 128, 1.0, 2},
+    {128, 128, 0.385, 64, 2.0}, {128, 128, 0.375, 128, 1.0, 2, 4.0},
     {128, 64, 0.31, 48, 2.5},   {64, 64, 0.22, 32, 2.0},
 };
 // float32: 256 x 256 is the ping-pong kernel, K-contiguous A and B only
@@ -252,7 +255,7 @@ struct Cand {
 };
 
 static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int occ, double eff,
-                  double sat)
+                  double sat, double fixed_us = 0.0)
 {
     Cand c{};
     const int BK = 8 * chunk_elems(p.dtype);
@@ -275,8 +278,8 @@ static Cand price(const Problem &p, const Chip &chip, int bm, int bn, int s, int
     // eff.  c is occ when the grid fills every slot, fewer when it is smaller.
     const int64_t per_cu = (c.units + chip.num_cus - 1) / chip.num_cus;
     const double conc = (double)std::min<int64_t>(occ, per_cu);
-    const double t_unit = std::max(conc, std::min(sat, (double)occ)) * (2.0 * bm * bn * (double)kps) /
-                          (flop_rate_cu(chip, p.dtype) * eff);
+    const double t_unit = std::max(conc, std::min(sat, (double)occ)) *
+                          ((2.0 * bm * bn * (double)kps) / (flop_rate_cu(chip, p.dtype) * eff) + fixed_us * 1e-6);
     // the tile kernel: waves of tiles, or its own HBM traffic (operands, and
     // the float32 partials it writes when K is split), whichever is longer
     const double partials = c.s > 1 ? (double)c.s * p.M * p.N * 4.0 : 0.0;
@@ -428,7 +431,7 @@ static int plan_mfma(const Problem &p, const Chip &chip, int occupancy, const tg
                                           : model_occupancy(p.dtype, ts.bm, ts.bn, vec, ts.kg));
         occ = std::max(1, occ);
         for (int j = 0; j < nsplit; ++j) {
-            Cand c = price(p, chip, ts.bm, ts.bn, splits[j], occ, ts.eff, ts.sat);
+            Cand c = price(p, chip, ts.bm, ts.bn, splits[j], occ, ts.eff, ts.sat, ts.fixed_us);
             c.kg = ts.kg;
             if (!have) {
                 best = c;

@@ -42,6 +42,8 @@ struct TileSpec {
                      // tile cannot hide its own load latency)
     int kg = 1;      // K groups: 2 or 4 sets of waves per workgroup, each over a part of
                      // the workgroup's K range, their sums added in LDS
+    double fixed_us = 0.0;  // time per workgroup beyond its K loop (the K groups' LDS
+                            // reduction, their fills), charged on top of the FLOP time
 };
 
 int tile_menu(int dtype, const TileSpec **out);       // vector-load tiles, largest first
