@@ -84,12 +84,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _K = "tiled_gemm_02_amd/csrc/kernels/"
 # The sources each kernel family's code comes from: its counters are void once
 # any of them changes.
-KERNEL_SOURCES = {   # instances.inc: the instantiations and launch shapes (e.g. the ring depth)
+# instances.inc: the instantiations and launch shapes (e.g. the ring depth); the
+# instance units (inst_*.hip): which tiles exist; plan.{h,cpp}: which kernel, tile
+# and split a workload gets (the softmax launch shape included)
+_PLAN = ["tiled_gemm_02_amd/csrc/plan.h", "tiled_gemm_02_amd/csrc/plan.cpp"]
+_INST = [_K + "inst_f16.hip", _K + "inst_bf16.hip", _K + "inst_f32.hip"]
+KERNEL_SOURCES = {
     "mfma": [_K + "common.hpp", _K + "instances.inc", _K + "mfma_gemm.hpp", _K + "mfma_gemm3.hpp",
-             _K + "mfma_pingpong.hpp"],
-    "skinny": [_K + "common.hpp", _K + "instances.inc", _K + "skinny.hpp"],
-    "gemv": [_K + "common.hpp", _K + "instances.inc", _K + "gemv.hpp"],
-    "softmax": [_K + "common.hpp", _K + "instances.inc", _K + "softmax.hpp"],
+             _K + "mfma_pingpong.hpp"] + _INST + _PLAN,
+    "skinny": [_K + "common.hpp", _K + "instances.inc", _K + "skinny.hpp"] + _INST + _PLAN,
+    "gemv": [_K + "common.hpp", _K + "instances.inc", _K + "gemv.hpp"] + _INST + _PLAN,
+    "softmax": [_K + "common.hpp", _K + "instances.inc", _K + "softmax.hpp"] + _INST + _PLAN,
 }
 
 

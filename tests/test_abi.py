@@ -147,9 +147,10 @@ def test_every_planned_16bit_tile_has_kernels(dtype):
 
 def test_every_planned_f32_register_tile_has_kernels():
     """The float32 register-staged tiles the planner may pick (128 x 128 with one
-    or two K groups, 64 x 64 with one or four) exist for all four layouts."""
+    or two K groups, 64 x 64 with one or four, 32 x 32 with four) exist for all
+    four layouts."""
     import re
     stubs = _kernel_stubs()
-    for bm, kg in [(128, 1), (128, 2), (64, 1), (64, 4)]:
+    for bm, kg in [(128, 1), (128, 2), (64, 1), (64, 4), (32, 4)]:
         found = set(re.findall(rf"tg::mfma_gemm_kernel<tg::F32, {bm}, {bm}, (\w+), (\w+), true, {kg}>", stubs))
         assert len(found) == 4, (bm, kg, found)

@@ -278,8 +278,8 @@ def test_two_k_groups_planned_and_sampled():
     assert r["ok"], r
 
 
-# float32 on the register-staged kernel with K groups (64 x 64 with four,
-# 128 x 128 with two; each group over consecutive 32-deep K steps, a group past
+# float32 on the register-staged kernel with K groups (64 x 64 and 32 x 32 with
+# four, 128 x 128 with two; each group over consecutive 32-deep K steps, a group past
 # the end of K loading zeros): every layout, ragged K, groups with no K, K splits,
 # alpha / beta and the epilogue
 F32_KG_CASES = [
@@ -291,6 +291,10 @@ F32_KG_CASES = [
     (264, 520, 100, NT, 128, 2, 1, "leaky_relu", 1.0, 0.0),
     (128, 128, 4, TN, 128, 2, 1, None, -1.25, 0.75),   # K = 4: group 1 empty
     (520, 264, 2000, TT, 128, 2, 3, None, 1.0, 0.0),
+    (256, 256, 256, NN, 32, 4, 1, None, 1.0, 0.0),
+    (36, 44, 1000, NT, 32, 4, 1, "leaky_relu", 0.5, -1.0),
+    (200, 136, 72, TN, 32, 4, 1, None, 1.0, 0.0),       # 3 steps over 4 groups
+    (264, 520, 1028, TT, 32, 4, 2, None, -1.25, 0.75),
 ]
 
 

@@ -192,11 +192,14 @@ def test_two_k_group_plans():
 
 
 def test_f32_k_group_plans():
-    """float32 on the register-staged kernel with K groups: 64 x 64 with four
-    groups where few tiles meet a long K (1024^3: 256 tiles, one workgroup of
-    sixteen waves each), 128 x 128 with two where the tiles fill the CUs once
-    (2048^3); the 256 x 256 ping-pong tile and large products keep one group."""
+    """float32 on the register-staged kernel with K groups: 32 x 32 with four
+    groups for the smallest products (256^3: 64 workgroups of sixteen waves, one
+    launch), 64 x 64 with four where few tiles meet a long K (1024^3: 256 tiles),
+    128 x 128 with two where the tiles fill the CUs once (2048^3); the 256 x 256
+    ping-pong tile and large products keep one group."""
     F = tg.TG_F32
+    p = tg.tg_plan_model(256, 256, 256, F)
+    assert (p["tile_m"], p["k_groups"], p["split_k"], p["workspace_bytes"]) == (32, 4, 1, 0), p
     p = tg.tg_plan_model(1024, 1024, 1024, F)
     assert (p["tile_m"], p["k_groups"], p["split_k"], p["workspace_bytes"]) == (64, 4, 1, 0), p
     p = tg.tg_plan_model(2048, 2048, 2048, F)

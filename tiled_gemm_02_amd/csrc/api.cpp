@@ -215,7 +215,7 @@ struct DeviceInfo {
     // taken once with this device current; null until then
     void *scratch_ptr = nullptr;
     // measured residency per (dtype, trans, tile, vec, K groups 1 / 2 / 4), 0 = not yet asked
-    int occ[3][4][8][2][3] = {};
+    int occ[3][4][9][2][3] = {};
     // benchmark-mode winners (tg_autotune) per problem, used by calls that
     // pass no options; guarded by g_tune_mu
     std::map<TuneKey, tg_options> tuned;
@@ -305,9 +305,9 @@ static hipError_t ws_alloc(DeviceInfo *d, void **ptr, size_t bytes, hipStream_t 
 static int tile_slot(int bm, int bn)
 {
     // index of the tile in a small fixed table used for the occupancy cache
-    static const int tiles[8][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64},
-                                    {64, 64},   {128, 256}, {64, 128},  {192, 256}};
-    for (int i = 0; i < 8; ++i)
+    static const int tiles[9][2] = {{256, 256}, {256, 128}, {128, 128}, {128, 64}, {64, 64},
+                                    {128, 256}, {64, 128},  {192, 256}, {32, 32}};
+    for (int i = 0; i < 9; ++i)
         if (tiles[i][0] == bm && tiles[i][1] == bn)
             return i;
     return -1;

@@ -49,12 +49,16 @@ static const TileSpec kTiles16[] = {
 // 8192^3 on MI355X: 137.6 TFLOP/s (NT, 256 x 256) and 126 (NN, 128 x 128) of
 // the 157.3 TFLOP/s float32 matrix peak.  With K groups (one workgroup per CU):
 // 128 x 128 x 2 groups at 2048^3 and 1024 x 1024 x 4096 split 4, 0.68-0.71;
-// 64 x 64 x 4 groups at 512^3 and 1024^3, 0.57.
+// 64 x 64 x 4 groups at 512^3 and 1024^3, 0.57; 32 x 32 x 4 groups (the
+// smallest products, one launch on up to 256 CUs) set to 0.30, which makes it
+// the plan for 128^3 to 512^3 (measured 256^3: 7.1 us against 10.1 us for
+// 64 x 64 x 4 groups split 4).
 static const TileSpec kTiles32[] = {
     {256, 256, 0.87, 160, 1.0},
     {128, 128, 0.80, 64, 2.0},
     {128, 128, 0.70, 128, 1.0, 2},
     {64, 64, 0.57, 128, 1.0, 4},
+    {32, 32, 0.30, 64, 1.0, 4},
     {64, 64, 0.48, 32, 2.0},
 };
 
