@@ -131,10 +131,11 @@ def test_every_planned_16bit_tile_has_kernels(dtype):
     """Every macro tile the planner may pick for 16-bit operands has its kernel
     compiled for all four layouts (256 x 256 and 192 x 256: the ping-pong
     kernel; the others: the four-wave LDS-DMA kernel, 128 x 128 also with two
-    K groups), so no plan can reach a launcher without an instance."""
+    K groups and 64 x 64 with four), so no plan can reach a launcher without an
+    instance."""
     import re
     stubs = _kernel_stubs()
-    for bm, bn, kg in [(256, 128, 1), (128, 128, 1), (128, 64, 1), (64, 64, 1), (128, 128, 2)]:
+    for bm, bn, kg in [(256, 128, 1), (128, 128, 1), (128, 64, 1), (64, 64, 1), (128, 128, 2), (64, 64, 4)]:
         found = set(re.findall(
             rf"tg::mfma_gemm3_kernel<tg::{dtype}, {bm}, {bn}, \d+, 2, 2, (\w+), (\w+), {kg}>", stubs))
         assert len(found) == 4, (bm, bn, kg, found)

@@ -241,12 +241,42 @@ def test_two_k_groups(case):
     assert r["ok"], (case, r)
 
 
+# 16-bit 64 x 64 tiles with four K groups (sixteen waves): the workgroup's
+# 64-deep stages dealt out in runs, a K tail as group 0's last stage, groups one
+# stage short (K = 136: 3 stages over 4 groups; K = 8: groups 1-3 with no K),
+# every layout, outer splits, alpha / beta and the epilogue
+KG4_CASES = [
+    (136, 200, 264, F16, NN, 1, None, 1.0, 0.0),
+    (200, 136, 8, BF16, NT, 1, None, 1.0, 0.0),
+    (96, 64, 136, F16, TN, 1, "leaky_relu", 1.0, 0.0),
+    (264, 520, 1032, BF16, TT, 1, None, 0.5, -1.0),
+    (520, 264, 4104, F16, NT, 3, None, 1.0, 0.0),
+    (128, 128, 520, BF16, NN, 1, "leaky_relu", -1.25, 0.75),
+]
+
+
+@pytest.mark.parametrize("case", KG4_CASES, ids=lambda c: "x".join(map(str, c[:3])) + f"-d{c[3]}-t{c[4]}-s{c[5]}")
+def test_four_k_groups(case):
+    import tiled_gemm_02_amd as tg
+    M, N, K, dtype, trans, split, epi, alpha, beta = case
+    _say("case four K groups", case)
+    p = make_problem(M, N, K, dtype, trans, "normal", seed=44)
+    opts = dict(tile_m=64, tile_n=64, split_k=split, k_groups=4)
+    pl = tg.tg_gemm_plan(M, N, K, dtype, trans, options=opts)
+    assert pl["k_groups"] == 4 and pl["split_k"] == split, pl
+    if alpha == 1.0 and beta == 0.0:
+        r, _, _ = check_full(p, epilogue=epi, options=opts)
+    else:
+        r, _, _ = check_scaled(p, alpha, beta, epilogue=epi, options=opts)
+    assert r["ok"], (case, r)
+
+
 def test_two_k_groups_refused_where_no_kernel_exists():
-    """Four groups for 16-bit, two for the float32 256 x 256 tile, 16-bit tiles
-    other than 128 x 128, the GEMV path and operands off the 16-byte grid have
+    """Four groups on 16-bit 128 x 128 tiles, two on the float32 256 x 256 tile,
+    16-bit 256 x 256 tiles, the GEMV path and operands off the 16-byte grid have
     no K-group kernel: the call fails; k_groups = 3 is an argument error."""
     import tiled_gemm_02_amd as tg
-    for dtype, shape, opts in [(F16, (256, 256, 256), dict(k_groups=4)),
+    for dtype, shape, opts in [(F16, (256, 256, 256), dict(tile_m=128, tile_n=128, k_groups=4)),
                                (F32, (256, 256, 256), dict(tile_m=256, tile_n=256, k_groups=2)),
                                (F16, (256, 256, 256), dict(tile_m=256, tile_n=256, k_groups=2)),
                                (F16, (1, 256, 256), dict(path=tg.TG_PATH_GEMV, k_groups=2)),

@@ -178,10 +178,9 @@ def test_two_k_group_plans():
     # other paths report one group
     assert tg.tg_plan_model(1, 8192, 8192, F)["k_groups"] == 1
     assert tg.tg_plan_model(8192, 128, 8192, F)["k_groups"] == 1
-    # no such kernel: four groups for 16-bit, stream-K, other paths, off-grid operands;
-    # bad values (a forced tile the model prices whatever it is)
-    for args, opts in [((1024, 1024, 4096, F), dict(k_groups=4)),
-                       ((1024, 1024, 4096, F), dict(k_groups=2, split_k=tg.TG_SPLIT_STREAM_K)),
+    # no such kernel: K groups with stream-K, other paths, off-grid operands; bad values
+    # (a forced tile the model prices whatever it is)
+    for args, opts in [((1024, 1024, 4096, F), dict(k_groups=2, split_k=tg.TG_SPLIT_STREAM_K)),
                        ((1, 1024, 4096, F), dict(k_groups=2, path=tg.TG_PATH_GEMV)),
                        ((300, 282, 130, F), dict(k_groups=2)),
                        ((1024, 1024, 4096, F), dict(k_groups=3)),

@@ -266,16 +266,18 @@ __device__ __forceinline__ u32x4 frag3_mn(uint32_t b0, uint32_t b1, int n0)
     return out;
 }
 
-// KG K groups per workgroup (1 or 2): with 2, the workgroup holds two sets of
+// KG K groups per workgroup (1, 2 or 4): the workgroup holds KG sets of
 // WGM x WGN waves, each running the pipeline above over its own part of the
-// workgroup's K range in its own LDS ring; at the end the second group's sums
-// are added to the first's through LDS (group 0 + group 1, a fixed order) and
-// the whole workgroup stores the tile.  It is a K split of two whose
-// reduction stays on the CU: no float32 partials in memory and no second
-// launch.  The groups meet at the same barriers, so both run the same number
-// of stages: group 0 takes the first ceil(klen / 16) * 8 elements of K (on the
-// 16-byte grid), group 1 the rest, and a group one whole stage short processes
-// an all-zero tail stage first.
+// workgroup's K range in its own LDS ring; at the end groups 1 .. KG-1 add
+// their sums to group 0's through LDS (in group order, a fixed order) and the
+// whole workgroup stores the tile.  It is a K split whose reduction stays on
+// the CU: no float32 partials in memory and no second launch.  The groups meet
+// at the same barriers, so all run the same number of stages: the workgroup's
+// 64-deep stages are dealt out in consecutive runs, ceil(n / KG) to the first
+// groups and one fewer to the rest, the partial stage of a K tail being the
+// last of group 0's run (groups 1 .. KG-1 start on the 16-byte grid, since K is
+// a multiple of 8); a group one whole stage short processes an all-zero tail
+// stage first, with no K to load.
 template <typename Tr, int BM, int BN, int S, int WGM, int WGN, bool TA, bool TB, int KG = 1>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArgs p)
 {
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
     // the host pass needs nothing but the signature for its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = typename Tr::T;
-    static_assert(KG == 1 || KG == 2, "one or two K groups");
+    static_assert(KG == 1 || KG == 2 || KG == 4, "1, 2 or 4 K groups");
     constexpr int NW = WGM * WGN;                         // waves per K group
     constexpr int NWALL = NW * KG;                        // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;           // wave sub-tile
@@ -313,17 +315,21 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
     const int z = blockIdx.y;
     const int kbeg_wg = z * p.kps;
     const int klen_wg = max(0, min(p.K, kbeg_wg + p.kps) - kbeg_wg);
-    const int klen0 = KG == 1 ? klen_wg : 8 * ((klen_wg + 15) / 16);   // group 0's share
-    const int kbeg = kbeg_wg + (kgrp ? klen0 : 0);
-    const int klen = kgrp ? klen_wg - klen0 : klen0;
-    // A partial last 64-deep stage (K not a multiple of 64) is processed
-    // first, as stage 0, through the masked register path; the whole stages
-    // follow, all copied by DMA.  Summation order over K is immaterial.  Both
-    // K groups process nst stages (group 0's count; group 1's share is at most
-    // 8 shorter, so it is short of it by at most one whole stage, which then
-    // becomes its tail with no valid K: zeros).
+    // this group's run of the workgroup's stages (KG = 1: all of them)
+    const int n64 = (klen_wg + kBK3 - 1) / kBK3;          // stages, the partial one included
+    const int short0 = (klen_wg % kBK3) ? kBK3 - klen_wg % kBK3 : 0;   // missing from the partial one
+    const int nst = (n64 + KG - 1) / KG;                   // stages every group processes
+    const int nhi = nst > 0 ? n64 - (nst - 1) * KG : KG;   // groups with nst stages of K
+    const int cnt = kgrp < nhi ? nst : nst - 1;            // this group's stages of K
+    const int first = kgrp < nhi ? kgrp * nst : nhi * nst + (kgrp - nhi) * (nst - 1);
+    const int kbeg = kbeg_wg + (kgrp == 0 ? 0 : kBK3 * first - short0);
+    const int klen = cnt <= 0 ? 0 : kBK3 * cnt - (kgrp == 0 ? short0 : 0);
+    // A partial 64-deep stage (group 0's last, when K is not a multiple of 64)
+    // is processed first, as stage 0, through the masked register path; the
+    // whole stages follow, all copied by DMA.  Summation order over K is
+    // immaterial.  A group with one stage fewer processes an all-zero stage 0
+    // the same way (no valid K).
     const int nfull = klen / kBK3;                // whole stages
-    const int nst = (klen0 + kBK3 - 1) / kBK3;    // stages processed
     const int has_tail = nst - nfull;             // 0 or 1
     OpA oa;
     OpB ob;
@@ -477,31 +483,35 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
     }
 
     // ---- epilogue: lane holds C[m][n .. n+3] of every 16 x 16 block
-    if constexpr (KG == 2) {
-        // group 1's sums join group 0's: each wave of group 1 parks its
+    if constexpr (KG > 1) {
+        // groups 1 .. KG-1 join group 0: each of their waves parks its
         // accumulators in LDS (16 bytes per lane, lane-linear: no bank
-        // conflicts) and the wave of group 0 with the same sub-tile adds them
-        static_assert(NW * FM * FN * 1024 <= LDS_BYTES, "reduction area");
+        // conflicts) and the wave of group 0 with the same sub-tile adds them,
+        // group by group
+        static_assert((KG - 1) * NW * FM * FN * 1024 <= LDS_BYTES, "reduction area");
         f32x4 *xs = (f32x4 *)lds_all + wave * (FM * FN * 64) + lane;
+        constexpr int GSTRIDE = NW * FM * FN * 64;   // f32x4 slots per group
         __syncthreads();   // every wave's last fragment reads are done
-        if (kgrp == 1) {
+        if (kgrp > 0) {
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    xs[(i * FN + j) * 64] = acc[i][j];
+                    xs[(kgrp - 1) * GSTRIDE + (i * FN + j) * 64] = acc[i][j];
         }
         __syncthreads();
         if (kgrp == 0) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+            for (int g = 1; g < KG; ++g)
 #pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const f32x4 v = xs[(i * FN + j) * 64];
+                for (int i = 0; i < FM; ++i)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[i][j][e] += v[e];
-                }
+                    for (int j = 0; j < FN; ++j) {
+                        const f32x4 v = xs[(g - 1) * GSTRIDE + (i * FN + j) * 64];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][j][e] += v[e];
+                    }
         }
     }
     // From here on the sums are group 0's; every wave of the workgroup meets
@@ -530,11 +540,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
             float *W = p.ws + (int64_t)z * p.M * p.N;
             const bool wvec = (p.N & 3) == 0;
             constexpr int RPI = 64 / CH;                     // rows per read instruction
-            constexpr int RW = BM / NWALL;                   // tile rows per wave
-            static_assert(RW % RPI == 0, "whole read instructions per wave");
+            constexpr int NI = BM / RPI;                     // read instructions per tile
+            static_assert(NI * RPI == BM, "whole read instructions per tile");
 #pragma unroll
-            for (int it = 0; it < RW / RPI; ++it) {
-                const int r = wave_all * RW + it * RPI + lane / CH, q = lane % CH;
+            for (int it = 0; it < (NI + NWALL - 1) / NWALL; ++it) {
+                const int ins = it * NWALL + wave_all;       // instruction of this wave (uniform)
+                if (NI % NWALL != 0 && ins >= NI)
+                    break;
+                const int r = ins * RPI + lane / CH, q = lane % CH;
                 const f32x4 v = *(const f32x4 *)(ct + r * (BN * 4) + ((q ^ (r & 15)) << 4));
                 const int m = m0 + r, n = n0 + 4 * q;
                 if (m < p.M && n < p.N) {
@@ -614,11 +627,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
             __syncthreads();
             const bool vec8 = (((uintptr_t)p.C) & 15) == 0 && (p.ldc & 7) == 0;
             constexpr int RPI = 64 / CH;                     // rows per read instruction
-            constexpr int RW = BM / NWALL;                   // tile rows per wave
-            static_assert(RW % RPI == 0, "whole read instructions per wave");
+            constexpr int NI = BM / RPI;                     // read instructions per tile
+            static_assert(NI * RPI == BM, "whole read instructions per tile");
 #pragma unroll
-            for (int it = 0; it < RW / RPI; ++it) {
-                const int r = wave_all * RW + it * RPI + lane / CH, q = lane % CH;
+            for (int it = 0; it < (NI + NWALL - 1) / NWALL; ++it) {
+                const int ins = it * NWALL + wave_all;       // instruction of this wave (uniform)
+                if (NI % NWALL != 0 && ins >= NI)
+                    break;
+                const int r = ins * RPI + lane / CH, q = lane % CH;
                 const u32x4 v = *(const u32x4 *)(ct + r * (BN * 2) + ((q ^ sw(r)) << 4));
                 const int m = m0 + r, n = n0 + 8 * q;
                 if (m < p.M && n < p.N) {

@@ -39,10 +39,14 @@ namespace tg {
 // (the reduction in LDS and both groups' fills), which decides against it for
 // short K (measured over 78 fp16 shapes x every tile and split: the picks with
 // the fixed charge average 1.009x the best candidate's time, 1.011x without).
+// 64 x 64 with four K groups (sixteen waves): small outputs with long K, where
+// each group's chain of stages is a quarter of the one-group kernel's
+// (256 x 256 x 65536 split 16: 35.8 against 40.4 us; 1024 x 1024 x 4096 in one
+// launch: 20.6 against 21.8 us for split 4).
 static const TileSpec kTiles16[] = {
     {256, 256, 0.50, 160, 1.0}, {192, 256, 0.42, 140, 1.0}, {256, 128, 0.355, 96, 1.0},
     {128, 128, 0.385, 64, 2.0}, {128, 128, 0.375, 128, 1.0, 2, 4.0},
-    {128, 64, 0.31, 48, 2.5},   {64, 64, 0.22, 32, 2.0},
+    {128, 64, 0.31, 48, 2.5},   {64, 64, 0.22, 32, 2.0},    {64, 64, 0.20, 128, 1.0, 4, 4.0},
 };
 // float32: 256 x 256 is the ping-pong kernel, K-contiguous A and B only
 // (tile_fits); the smaller tiles are the register-staged kernel.  Measured at
