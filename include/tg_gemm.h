@@ -131,9 +131,10 @@ typedef struct tg_options {
     int32_t k_groups; /* macro-tile path: 0 = planner's choice (1 when the tile is
                          forced), 1 = one group of waves per workgroup, 2 or 4 = that many
                          groups of waves per workgroup, each taking a consecutive part of
-                         the workgroup's K range, their sums added in LDS (16-bit 128 x 128
-                         tiles: 2; float32 128 x 128: 2, 64 x 64: 4); other values are
-                         TG_ERR_ARG, a count no kernel offers TG_ERR_UNSUPPORTED */
+                         the workgroup's K range, their sums added in LDS (16-bit: 128 x 128
+                         with 2, 64 x 64 with 4; float32: 128 x 128 with 2, 64 x 64 and
+                         32 x 32 with 4); other values are TG_ERR_ARG, a count no kernel
+                         offers for the operands TG_ERR_UNSUPPORTED */
 } tg_options;
 
 /* What the planner decided, and the quantization figures behind it. */
