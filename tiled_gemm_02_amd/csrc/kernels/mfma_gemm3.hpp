@@ -52,7 +52,7 @@ namespace tg {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBK3 = 64;   // K per stage (16-bit elements) of the pipelined kernel
+constexpr int kBK3 = 64;   // K per stage (16-bit elements) of the pipelined kernel, by default
 
 // Chunk swizzle of a K-contiguous LDS row of KCH 16-byte chunks (KCH = 8:
 // 128-byte rows, 64-deep stages; KCH = 4: 64-byte rows, 32-deep stages).  SW
@@ -278,7 +278,11 @@ __device__ __forceinline__ u32x4 frag3_mn(uint32_t b0, uint32_t b1, int n0)
 // last of group 0's run (groups 1 .. KG-1 start on the 16-byte grid, since K is
 // a multiple of 8); a group one whole stage short processes an all-zero tail
 // stage first, with no K to load.
-template <typename Tr, int BM, int BN, int S, int WGM, int WGN, bool TA, bool TB, int KG = 1>
+//
+// BKS: K depth of a stage, 64 (every K-contiguous row contributes a whole
+// 128-byte line per stage) or 32 (half-line rows, twice the stages in the same
+// LDS, so more of them in flight); a stage is BKS / 32 blocks of 32-deep MFMAs.
+template <typename Tr, int BM, int BN, int S, int WGM, int WGN, bool TA, bool TB, int KG = 1, int BKS = kBK3>
 __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArgs p)
 {
     // The LDS-DMA and transposed-read builtins exist on the device side only;
@@ -286,12 +290,15 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = typename Tr::T;
     static_assert(KG == 1 || KG == 2 || KG == 4, "1, 2 or 4 K groups");
+    static_assert(BKS == 32 || BKS == 64, "32- or 64-deep stages");
+    constexpr int KB = BKS / 32;                          // 32-deep K blocks per stage
+    constexpr int KCH = BKS / 8;                          // 16-byte chunks per K-contiguous row
     constexpr int NW = WGM * WGN;                         // waves per K group
     constexpr int NWALL = NW * KG;                        // waves per workgroup
     constexpr int WM = BM / WGM, WN = BN / WGN;           // wave sub-tile
     constexpr int FM = WM / 16, FN = WN / 16;
-    using OpA = Dma3<BM, TA, NW>;
-    using OpB = Dma3<BN, !TB, NW>;
+    using OpA = Dma3<BM, TA, NW, BKS>;
+    using OpB = Dma3<BN, !TB, NW, BKS>;
     constexpr int A_BYTES = OpA::BYTES, B_BYTES = OpB::BYTES;
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int NDMA = OpA::PER_WAVE + OpB::PER_WAVE;  // copies per wave per stage
@@ -316,20 +323,20 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
     const int kbeg_wg = z * p.kps;
     const int klen_wg = max(0, min(p.K, kbeg_wg + p.kps) - kbeg_wg);
     // this group's run of the workgroup's stages (KG = 1: all of them)
-    const int n64 = (klen_wg + kBK3 - 1) / kBK3;          // stages, the partial one included
-    const int short0 = (klen_wg % kBK3) ? kBK3 - klen_wg % kBK3 : 0;   // missing from the partial one
+    const int n64 = (klen_wg + BKS - 1) / BKS;            // stages, the partial one included
+    const int short0 = (klen_wg % BKS) ? BKS - klen_wg % BKS : 0;   // missing from the partial one
     const int nst = (n64 + KG - 1) / KG;                   // stages every group processes
     const int nhi = nst > 0 ? n64 - (nst - 1) * KG : KG;   // groups with nst stages of K
     const int cnt = kgrp < nhi ? nst : nst - 1;            // this group's stages of K
     const int first = kgrp < nhi ? kgrp * nst : nhi * nst + (kgrp - nhi) * (nst - 1);
-    const int kbeg = kbeg_wg + (kgrp == 0 ? 0 : kBK3 * first - short0);
-    const int klen = cnt <= 0 ? 0 : kBK3 * cnt - (kgrp == 0 ? short0 : 0);
-    // A partial 64-deep stage (group 0's last, when K is not a multiple of 64)
+    const int kbeg = kbeg_wg + (kgrp == 0 ? 0 : BKS * first - short0);
+    const int klen = cnt <= 0 ? 0 : BKS * cnt - (kgrp == 0 ? short0 : 0);
+    // A partial stage (group 0's last, when K is not a multiple of BKS)
     // is processed first, as stage 0, through the masked register path; the
     // whole stages follow, all copied by DMA.  Summation order over K is
     // immaterial.  A group with one stage fewer processes an all-zero stage 0
     // the same way (no valid K).
-    const int nfull = klen / kBK3;                // whole stages
+    const int nfull = klen / BKS;                 // whole stages
     const int has_tail = nst - nfull;             // 0 or 1
     OpA oa;
     OpB ob;
@@ -343,7 +350,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
         const int slot = t % S;
         if (has_tail && t == 0) {
             char *st = lds + slot * STAGE;
-            const int krel = klen - nfull * kBK3;
+            const int krel = klen - nfull * BKS;
             oa.tail(nfull, krel, st, wave, lane);
             ob.tail(nfull, krel, st + A_BYTES, wave, lane);
         } else {
@@ -377,9 +384,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
 
     const int fr = lane & 15, fg = lane >> 4;
     // per-lane bases of the transposed reads, by (K block, half), at stage 0
-    uint32_t mnA[2][2], mnB[2][2];
+    uint32_t mnA[KB][2], mnB[KB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             mnA[kb][h] = mn3_base<BM / 8>(lds_base, kb, h, lane);
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
         }
     auto read_a = [&](const char *st, int kb, int i) -> u32x4 {
         if constexpr (!TA) {
-            return frag3_kc(st, wm * WM + 16 * i, kb, lane);
+            return frag3_kc<KCH>(st, wm * WM + 16 * i, kb, lane);
         } else {
             const uint32_t so = (uint32_t)(st - lds);
             return frag3_mn<BM / 8>(mnA[kb][0] + so, mnA[kb][1] + so, wm * WM + 16 * i);
@@ -395,7 +402,7 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
     };
     auto read_b = [&](const char *st, int kb, int j) -> u32x4 {
         if constexpr (TB) {
-            return frag3_kc(st + A_BYTES, wn * WN + 16 * j, kb, lane);
+            return frag3_kc<KCH>(st + A_BYTES, wn * WN + 16 * j, kb, lane);
         } else {
             const uint32_t so = (uint32_t)(st - lds);
             return frag3_mn<BN / 8>(mnB[kb][0] + so, mnB[kb][1] + so, wn * WN + 16 * j);
@@ -434,10 +441,11 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
         // just released are spread one per row over the rest of the block, so
         // the matrix unit is never left waiting behind a burst of copy issues.
         auto body = [&](int t, int kb, const u32x4 *fb, u32x4 *nb, bool more) {
-            const int tn1 = kb ? t + 1 : t;        // stage of the next block
-            const int kbn = kb ? 0 : 1;
+            const bool last = kb == KB - 1;        // the next block starts stage t + 1
+            const int tn1 = last ? t + 1 : t;      // stage of the next block
+            const int kbn = last ? 0 : kb + 1;
             const char *nst_p = lds + (tn1 % S) * STAGE;
-            const bool refill = more && kb == 1 && t + S < nst;
+            const bool refill = more && last && t + S < nst;
             const uint32_t rslot = lds_base + ((t + S) % S) * STAGE;
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -445,12 +453,12 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
                 for (int j = 0; j < FN; ++j)
                     mfma_tied<Tr>(acc[i][j], fb[j], fa[i]);
                 if (more) {
-                    if (i == 0 && kb == 1) {
+                    if (i == 0 && last) {
                         // stages up to t + S - 1 have been issued
                         wait_stage(t + 1, min(nst - 1, t + S - 1));
                         lds_barrier();
                     }
-                    if (kb == 1) {
+                    if (last) {
                         // copies q = i, i + FM, ... of stage t + S (DMA: t + S >= 1)
 #pragma unroll
                         for (int q = i; q < NDMA; q += FM) {
@@ -473,11 +481,20 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        // Two K blocks (one stage) per trip; the B fragments ping-pong between
-        // two register sets, so every accumulator keeps one register home.
-        for (int t = 0; t < nst; ++t) {
-            body(t, 0, fb0, fb1, true);
-            body(t, 1, fb1, fb0, t + 1 < nst);
+        // Two K blocks per trip (one 64-deep stage, or two 32-deep ones); the B
+        // fragments ping-pong between two register sets, so every accumulator
+        // keeps one register home.
+        if constexpr (KB == 2) {
+            for (int t = 0; t < nst; ++t) {
+                body(t, 0, fb0, fb1, true);
+                body(t, 1, fb1, fb0, t + 1 < nst);
+            }
+        } else {
+            for (int t = 0; t < nst; t += 2) {
+                body(t, 0, fb0, fb1, t + 1 < nst);
+                if (t + 1 < nst)
+                    body(t + 1, 0, fb1, fb0, t + 2 < nst);
+            }
         }
         mfma_drain();
     }
