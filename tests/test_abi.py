@@ -137,7 +137,7 @@ def test_every_planned_16bit_tile_has_kernels(dtype):
     stubs = _kernel_stubs()
     for bm, bn, kg in [(256, 128, 1), (128, 128, 1), (128, 64, 1), (64, 64, 1), (128, 128, 2), (64, 64, 4)]:
         found = set(re.findall(
-            rf"tg::mfma_gemm3_kernel<tg::{dtype}, {bm}, {bn}, \d+, 2, 2, (\w+), (\w+), {kg}>", stubs))
+            rf"tg::mfma_gemm3_kernel<tg::{dtype}, {bm}, {bn}, \d+, 2, 2, (\w+), (\w+), {kg}, \d+>", stubs))
         assert len(found) == 4, (bm, bn, kg, found)
     # the ping-pong tiles in two forms: whole tile to C (1), K splits and old C (0)
     for bm in (256, 192):
