@@ -323,10 +323,10 @@ __global__ __launch_bounds__(64 * WGM * WGN * KG) void mfma_gemm3_kernel(MfmaArg
     const int kbeg_wg = z * p.kps;
     const int klen_wg = max(0, min(p.K, kbeg_wg + p.kps) - kbeg_wg);
     // this group's run of the workgroup's stages (KG = 1: all of them)
-    const int n64 = (klen_wg + BKS - 1) / BKS;            // stages, the partial one included
+    const int nstg = (klen_wg + BKS - 1) / BKS;           // stages, the partial one included
     const int short0 = (klen_wg % BKS) ? BKS - klen_wg % BKS : 0;   // missing from the partial one
-    const int nst = (n64 + KG - 1) / KG;                   // stages every group processes
-    const int nhi = nst > 0 ? n64 - (nst - 1) * KG : KG;   // groups with nst stages of K
+    const int nst = (nstg + KG - 1) / KG;                  // stages every group processes
+    const int nhi = nst > 0 ? nstg - (nst - 1) * KG : KG;  // groups with nst stages of K
     const int cnt = kgrp < nhi ? nst : nst - 1;            // this group's stages of K
     const int first = kgrp < nhi ? kgrp * nst : nhi * nst + (kgrp - nhi) * (nst - 1);
     const int kbeg = kbeg_wg + (kgrp == 0 ? 0 : BKS * first - short0);

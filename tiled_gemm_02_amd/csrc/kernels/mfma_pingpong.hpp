@@ -90,8 +90,9 @@ __device__ __forceinline__ uint32_t mn32_base(uint32_t st, int ks, int h, int la
 // EP selects the epilogue the instance carries: 1 = the whole tile to a 16-bit
 // C without old C (no K split, beta = 0: the LDS-staged row stores and nothing
 // else), 0 = every other case (K-split partials, old C, float32).  The launcher
-// picks the instance from the call, so no kernel holds code it cannot run; the
-// unused epilogues cost the whole-tile kernel about 1 % at 8192^3 when present.
+// picks the instance from the call, so no kernel holds code it cannot run (with
+// every epilogue in one kernel, adding the staged split partials had cost 8192^3
+// about 1 %, with the K loop unchanged).
 template <typename Tr, int S, int MI, bool TA, bool TB, bool SK = false, int BM = 256, int EP = 0>
 __global__ __launch_bounds__(512) void mfma_pingpong_kernel(MfmaArgs p)
 {
