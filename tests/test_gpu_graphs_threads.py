@@ -29,7 +29,8 @@ def test_graph_capture_replays_match_eager():
     dev = torch.device("cuda:0")
     # a whole-tile product, a split-K product (reduction kernel), a stream-K
     # product (fix-up kernel), 192 x 256 tiles, 128 x 128 tiles with two K
-    # groups (alone, and with a K split), a float32 NN product through
+    # groups (alone, and with a K split), 64 x 64 tiles with four (16-bit, with
+    # a K split) and float32 32 x 32 tiles with four, a float32 NN product through
     # its transposing copy, skinny and GEMV split-K products (reduction
     # kernels) and a row softmax, all with one caller workspace
     probs = [(make_problem(1024, 1024, 1024, F16, NN, "normal", seed=71), None),
@@ -42,6 +43,9 @@ def test_graph_capture_replays_match_eager():
              (make_problem(768, 1024, 1024, F16, NN, "normal", seed=75), dict(tile_m=192, tile_n=256)),
              (make_problem(2304, 1536, 1024, F16, NN, "normal", seed=79), dict(k_groups=2)),
              (make_problem(520, 392, 4104, BF16, NT, "normal", seed=80), dict(k_groups=2, split_k=3)),
+             (make_problem(256, 256, 8192, F16, NN, "normal", seed=81),
+              dict(tile_m=64, tile_n=64, k_groups=4, split_k=4)),
+             (make_problem(256, 256, 256, F32, NN, "normal", seed=82), dict(tile_m=32, tile_n=32, k_groups=4)),
              (make_problem(1024, 1024, 1024, F32, NN, "normal", seed=76), dict(tile_m=256, tile_n=256))]
     assert tg.tg_gemm_plan(1024, 1024, 1024, tg.TG_F32, tg.TG_NN,
                            options=dict(tile_m=256, tile_n=256))["vector_io"] == 3

@@ -67,6 +67,9 @@ PAIRS = [
     (((1031, 1029, 1027), F16, NN, None, None), ((777, 1003, 1001), F16, NT, None, None)),
     # stream-K pieces (64 workgroups: 32 MiB), then whole tiles split two ways
     (((256, 512, 1024), F16, NN, {"split_k": -1}, None), ((256, 256, 512), F16, NN, {"split_k": 2}, None)),
+    # K groups inside the workgroups with a K split across them: two groups, then four
+    (((520, 392, 4104), BF16, NT, {"k_groups": 2, "split_k": 3}, None),
+     ((264, 264, 1032), F16, NN, {"tile_m": 64, "tile_n": 64, "k_groups": 4, "split_k": 2}, "leaky_relu")),
 ]
 
 
