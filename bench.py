@@ -421,9 +421,9 @@ def traffic_summarize(root: str):
              f"{COPY_BYTES >> 20} MiB device copy (factors {k_fetch:.3f} fetch, {k_write:.3f} write).", "",
              "Commands (repository root, one MI355X; NAME is each workload below, and `copy`):", "",
              "```",
-             "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/traffic/NAME_fetch -o run --output-format csv -- python3 bench.py --traffic-kernel NAME",
-             "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/traffic/NAME_write -o run --output-format csv -- python3 bench.py --traffic-kernel NAME",
-             "python3 bench.py --traffic-summarize gpurun_out/traffic",
+             f"rocprofv3 --pmc FETCH_SIZE -d {root}/NAME_fetch -o run --output-format csv -- python3 bench.py --traffic-kernel NAME",
+             f"rocprofv3 --pmc WRITE_SIZE -d {root}/NAME_write -o run --output-format csv -- python3 bench.py --traffic-kernel NAME",
+             f"python3 bench.py --traffic-summarize {root}",
              "```", "",
              "| Workload | Kernel | Fetch (MiB) | Write (MiB) | Total (MiB) | Algorithmic (MiB) | Ratio |",
              "|---|---|---|---|---|---|---|"]
