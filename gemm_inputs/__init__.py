@@ -227,6 +227,11 @@ WORKLOADS = {
     # the full BLAS statement C = alpha A.B + beta C_old (C_old from make_c_old, seed 1)
     "f16_8192_alpha_beta": dict(M=8192, N=8192, K=8192, dtype=F16, trans=NN, dist="normal", seed=1,
                                 alpha=0.5, beta=1.0),
+    # points of the M = 2304, K = 4096 sweep on the four-wave kernel's tiles (two K
+    # groups on 128 x 128, 128 x 64, 128 x 128), for counter passes
+    "f16_2304x1536x4096": dict(M=2304, N=1536, K=4096, dtype=F16, trans=NN, dist="normal", seed=1),
+    "f16_2304x2560x4096": dict(M=2304, N=2560, K=4096, dtype=F16, trans=NN, dist="normal", seed=1),
+    "f16_2304x3072x4096": dict(M=2304, N=3072, K=4096, dtype=F16, trans=NN, dist="normal", seed=1),
 }
 
 
