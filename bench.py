@@ -700,6 +700,84 @@ def sweep(out_path: str, step: int, reps: int = 20, tune: bool = False):
     print("\n".join(lines))
 
 
+def planner_check(out_path: str, reps: int = 10):
+    """How close the planner's pick is to the fastest plan the library offers, over
+    assorted fp16 products: M, N from 1024 to 8192 with K = 1024, 4096 and 8192 (NN)
+    and four NT shapes.  At each shape the planner's plan and every macro tile (one K
+    group, and the K-group forms) at K splits 1, 2 and 4 are timed back to back
+    (`reps` calls between two events, after untimed calls that keep the GPU busy:
+    a quarter second before the first timing, 20 ms before each later one), with one
+    persistent workspace; plans needing more workspace are skipped."""
+    import torch
+    import tiled_gemm_02_amd as tg
+    device = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(device)
+    g = torch.Generator(device=device).manual_seed(6)
+    ws_bytes = 256 << 20
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    tg.tune_cache_clear()
+    tiles = [(256, 256, 1), (192, 256, 1), (256, 128, 1), (128, 128, 1), (128, 128, 2), (128, 64, 1),
+             (64, 64, 1), (64, 64, 4)]
+    cands = [None] + [dict(path=tg.TG_PATH_MFMA, tile_m=bm, tile_n=bn, k_groups=kg, split_k=sp)
+                      for bm, bn, kg in tiles for sp in (1, 2, 4)]
+    shapes = [(M, N, K, tg.TG_NN) for (M, N) in [(1024, 1024), (1024, 3072), (2048, 2048), (3072, 2048),
+                                                  (3072, 3072), (4096, 2048), (4096, 4096), (6144, 4096),
+                                                  (5120, 5120), (8192, 4096), (1536, 6144), (2560, 2560)]
+              for K in (1024, 4096, 8192)]
+    shapes += [(4096, 4096, 4096, tg.TG_NT), (2304, 2048, 4096, tg.TG_NT), (3072, 3072, 2048, tg.TG_NT),
+               (2048, 2048, 8192, tg.TG_NT)]
+    first = [True]
+    rows = []
+    for M, N, K, tr in shapes:
+        A = (torch.randn((M, K), generator=g, device=device) / math.sqrt(K)).half()
+        B = (torch.randn((N, K) if tr == tg.TG_NT else (K, N), generator=g, device=device) / math.sqrt(K)).half()
+        C = torch.empty((M, N), dtype=torch.float16, device=device)
+        times = []
+        for o in cands:
+            try:
+                pl = tg.tg_gemm_plan(M, N, K, tg.TG_F16, tr, options=o)
+            except tg.TgError:
+                continue
+            if pl["workspace_bytes"] > ws_bytes:
+                continue
+
+            def call(_i=0):
+                tg.gemm(A, B, trans_b=tr == tg.TG_NT, out=C, options=o, workspace=ws, stream=stream.cuda_stream)
+            settle(call, device, SETTLE_S if first[0] else 0.02)
+            first[0] = False
+            times.append((time_back_to_back(call, stream, reps), o is None, pl))
+        # the planner's plan is also among the forced candidates (unless it splits K
+        # another way): its time is the best of those timings, since the first
+        # timing of a shape comes straight after the previous shape's
+        pp = [t for t in times if t[1]][0][2]
+        same = [t for t in times if (t[2]["tile_m"], t[2]["tile_n"], t[2]["split_k"], t[2]["k_groups"]) ==
+                (pp["tile_m"], pp["tile_n"], pp["split_k"], pp["k_groups"])]
+        planner = min(same, key=lambda t: t[0])
+        best = min(times, key=lambda t: t[0])
+        rows.append((M, N, K, tr, planner, best, planner[0] / best[0]))
+        log(f"{M}x{N}x{K} {'NT' if tr == tg.TG_NT else 'NN'}: planner {tile_label(planner[2])} "
+            f"s{planner[2]['split_k']} {planner[0] * 1e3:.1f} us, best {tile_label(best[2])} "
+            f"s{best[2]['split_k']} {best[0] * 1e3:.1f} us")
+        del A, B, C
+    ratios = sorted(r[6] for r in rows)
+    mean = sum(ratios) / len(ratios)
+    behind = sum(1 for q in ratios if q > 1.05)
+    lines = ["# The planner's pick against every plan, fp16 products", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"python3 bench.py --planner-check {out_path}", "```", "",
+             f"{len(rows)} shapes.  Planner time / best time: mean {mean:.4f}, median "
+             f"{ratios[len(ratios) // 2]:.4f}, worst {ratios[-1]:.3f}; more than 5 % behind at {behind}.", "",
+             "| M | N | K | Layout | Planner plan | us | Best plan | us | Planner / best |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for M, N, K, tr, pl, b, q in rows:
+        lines.append(f"| {M} | {N} | {K} | {'NT' if tr == tg.TG_NT else 'NN'} | {tile_label(pl[2])} split "
+                     f"{pl[2]['split_k']} | {pl[0] * 1e3:.1f} | {tile_label(b[2])} split {b[2]['split_k']} | "
+                     f"{b[0] * 1e3:.1f} | {q:.3f} |")
+    lines.append("")
+    open(out_path, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def align_sweep(out_path: str, reps: int = 20):
     """fp16 NN products of about 4096^3 with one size off the 16-byte grid: K = 4096 + d
     (rows of A off the grid) and M = N = 4096 + d (ragged tiles and rows of B and C off
@@ -874,6 +952,9 @@ def main():
     ap.add_argument("--sweep-step", type=int, default=8)
     ap.add_argument("--sweep-tune", action="store_true",
                     help="with --sweep: also time tg_autotune's best plan at every point")
+    ap.add_argument("--planner-check", default=None,
+                    help="time the planner's pick against every plan on assorted fp16 products, "
+                         "write the table to this file, then exit")
     ap.add_argument("--align-sweep", default=None,
                     help="run the K-alignment sweep, write its summary to this file, then exit")
     ap.add_argument("--stream-k-compare", default=None,
@@ -917,6 +998,9 @@ def main():
         return
     if args.align_sweep:
         align_sweep(args.align_sweep)
+        return
+    if args.planner_check:
+        planner_check(args.planner_check)
         return
     if args.softmax_sweep:
         softmax_sweep(args.softmax_sweep)
